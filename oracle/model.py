@@ -1,0 +1,428 @@
+"""The edge convolution, its energy readout and its force backward (float64).
+
+TEST INFRASTRUCTURE ONLY (oracle; never used by the product path).
+
+What the pages fix, and where:
+
+* per-edge radial basis feeding a per-degree, per-channel projection
+  (E, 4, 32) -> (E, 4, 64) -> (E, 256): "deepmd-kit PR #6108", What;
+* degrees l <= 3 and FP32 on the device: "deepmd-kit PR #2", Implementation
+  and scope (the checked lmax3 FP32 layout);
+* the input-gradient (force) backward of the edge chain, computed per edge
+  cohort: "deepmd-kit PR #2", Summary and Implementation and scope;
+  "FastMACE rewrite screens", OPT6-T02 chunked_conv_backward;
+* no float atomics in the per-atom sums: "FastMACE rewrite screens",
+  OPT-T02 stage D (rejected because its per-atom reduction needs atomics)
+  and OPT4-T02 polar_graph_sums.
+
+The synthetic model itself (no page defines one) is the plainest reading of
+the workloads' description, written out below.  For an edge e = (i, j, n)
+with vector d = x_j - x_i + n L, length r and direction u = d / r:
+
+    b_n(r)  = sin(n pi r / rc) / r * env(r / rc),   n = 1..32
+    env(x)  = 1 - 28 x^6 + 48 x^7 - 21 x^8  (x < 1), 0 otherwise
+              (polynomial envelope of exponent p = 6)
+    z1 = b W1, s1 = silu(z1), z2 = s1 W2, s2 = silu(z2), R = s2 W3
+              (weights of the ordered pair (Z_i, Z_j), x W with W [in, out],
+               no biases, R column l*C + c)
+    Y_lm(u)   real, component-normalised, l <= 3 (see ``sph``)
+    A_{i,lm,c} = sum_{e in row i} R_{e,l,c} Y_{e,lm} h_{Z_j,c}
+    E_i = sum_c w_c sum_lm A_{i,lm,c}^2,   E = sum_i E_i
+
+and the backward g_e = dE/dd_e, F_i = sum_{e in row i} (g_e - g_rev(e)).
+
+Pins (tests/test_oracle_*.py): envelope closed-form conditions; basis
+orthogonality by quadrature and its r-derivative against finite differences;
+a special-weight network that reduces to a scalar closed form; the dimer
+closed form; the convention-free addition-theorem double sum for E_i;
+perfect-crystal site-symmetry zeros; rotation / translation invariance;
+force equivariance; central finite differences of E; sum F = 0; the folded
+and reassociated last-layer forms; virial against a strain derivative.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+from . import sph
+from .neighbors import CSR, edge_vectors, neighbors_celllist
+
+N_BASIS = 32
+LIDX = sph.l_of_index()  # degree l of each flat lm index
+
+
+# ----------------------------------------------------------------- radial part
+def envelope(x: np.ndarray) -> np.ndarray:
+    """Polynomial cutoff envelope, exponent p = 6 (zero value, slope and
+    curvature at x = 1)."""
+    x = np.asarray(x, np.float64)
+    u = 1.0 - 28.0 * x**6 + 48.0 * x**7 - 21.0 * x**8
+    return np.where(x < 1.0, u, 0.0)
+
+
+def envelope_d(x: np.ndarray) -> np.ndarray:
+    """d env / dx = -168 x^5 (1 - x)^2 for x < 1."""
+    x = np.asarray(x, np.float64)
+    return np.where(x < 1.0, -168.0 * x**5 * (1.0 - x) ** 2, 0.0)
+
+
+def radial_basis(r: np.ndarray, rc: float, n_basis: int = N_BASIS, deriv: bool = False):
+    """b_n(r) = sin(n pi r / rc) / r * env(r / rc), n = 1..n_basis; optionally db/dr."""
+    r = np.asarray(r, np.float64)
+    n = np.arange(1, n_basis + 1, dtype=np.float64)
+    x = r / rc
+    u = envelope(x)
+    arg = (n[None, :] * math.pi / rc) * r[:, None]
+    s = np.sin(arg)
+    b = s / r[:, None] * u[:, None]
+    if not deriv:
+        return b
+    c = np.cos(arg)
+    db = ((n[None, :] * math.pi / rc) * c / r[:, None] - s / (r[:, None] ** 2)) * u[:, None] \
+        + (s / r[:, None]) * (envelope_d(x) / rc)[:, None]
+    return b, db
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def silu_d(z):
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def radial_mlp(b, W1, W2, W3):
+    """Three linear layers, SiLU after the first two.  Returns all activations."""
+    z1 = b @ W1
+    s1 = silu(z1)
+    z2 = s1 @ W2
+    s2 = silu(z2)
+    R = s2 @ W3
+    return z1, s1, z2, s2, R
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def geometry(d: np.ndarray):
+    """r = sqrt((dx*dx + dy*dy) + dz*dz), u = d / r."""
+    r2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+    r = np.sqrt(r2)
+    return r, d / r[:, None]
+
+
+def pair_index(species, csr: CSR, n_species: int):
+    recv = csr.receivers()
+    return species[recv].astype(np.int64) * n_species + species[csr.col].astype(np.int64)
+
+
+def _blocks(row_ptr: np.ndarray, max_edges: int = 16384):
+    """Receiver ranges [i0, i1) whose edges fit a block."""
+    n = len(row_ptr) - 1
+    i0 = 0
+    rp = row_ptr.astype(np.int64)
+    while i0 < n:
+        i1 = int(np.searchsorted(rp, rp[i0] + max_edges, side="right")) - 1
+        i1 = max(i1, i0 + 1)
+        i1 = min(i1, n)
+        yield i0, i1
+        i0 = i1
+
+
+def _edge_stage(d, pairs, model, rc, want_grad=False):
+    """Per-edge basis, harmonics and network activations for a block of edges."""
+    r, u = geometry(d)
+    if want_grad:
+        b, db = radial_basis(r, rc, deriv=True)
+        Y, dY = sph.real_sph(u, grad=True)
+    else:
+        b = radial_basis(r, rc)
+        Y = sph.real_sph(u)
+        db = dY = None
+    C = model.channels
+    ne = len(d)
+    acts = {k: np.zeros((ne, w)) for k, w in (("z1", 64), ("s1", 64), ("z2", 64), ("s2", 64), ("R", 4 * C))}
+    for p in np.unique(pairs):
+        sel = pairs == p
+        z1, s1, z2, s2, R = radial_mlp(b[sel], _f64(model.W1[p]), _f64(model.W2[p]), _f64(model.W3[p]))
+        for k, v in (("z1", z1), ("s1", s1), ("z2", z2), ("s2", s2), ("R", R)):
+            acts[k][sel] = v
+    return dict(r=r, u=u, b=b, db=db, Y=Y, dY=dY, **acts)
+
+
+def _segment_sum(vals, local_recv, n_rows):
+    """Sum edge rows into receiver rows (edges are receiver-sorted)."""
+    out = np.zeros((n_rows,) + vals.shape[1:])
+    if len(vals) == 0:
+        return out
+    starts = np.flatnonzero(np.r_[True, local_recv[1:] != local_recv[:-1]])
+    out[local_recv[starts]] = np.add.reduceat(vals, starts, axis=0)
+    return out
+
+
+# ------------------------------------------------------------------ forward
+def forward_edges(d, csr: CSR, species, model, keep_edges: bool = False):
+    """A [N, 16, C], E_i [N], E from edge vectors d [E, 3] on a fixed CSR."""
+    n = len(csr.row_ptr) - 1
+    C = model.channels
+    rc = model.cutoff
+    h = _f64(model.emb)
+    w = _f64(model.w_read)
+    pairs = pair_index(species, csr, model.n_species)
+    recv = csr.receivers()
+    A = np.zeros((n, 16, C))
+    edges = {} if keep_edges else None
+    rp = csr.row_ptr.astype(np.int64)
+    for i0, i1 in _blocks(csr.row_ptr):
+        e0, e1 = rp[i0], rp[i1]
+        if e1 == e0:
+            continue
+        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, rc)
+        R = st["R"].reshape(-1, 4, C)
+        hj = h[species[csr.col[e0:e1]]]
+        msg = R[:, LIDX, :] * st["Y"][:, :, None] * hj[:, None, :]
+        A[i0:i1] = _segment_sum(msg, recv[e0:e1] - i0, i1 - i0)
+        if keep_edges:
+            for k in ("r", "b", "Y", "R"):
+                edges.setdefault(k, []).append(st[k])
+    Ei = (A**2).sum(axis=1) @ w
+    E = math.fsum(Ei.tolist())
+    out = dict(A=A, Ei=Ei, E=E)
+    if keep_edges:
+        out["edges"] = {k: np.concatenate(v) for k, v in edges.items()}
+    return out
+
+
+# ------------------------------------------------------------------ backward
+def backward_edges(d, csr: CSR, species, model, A):
+    """g_e = dE/dd_e [E, 3] given the complete per-atom A."""
+    C = model.channels
+    rc = model.cutoff
+    h = _f64(model.emb)
+    w = _f64(model.w_read)
+    Abar = 2.0 * w[None, None, :] * A  # dE/dA
+    pairs = pair_index(species, csr, model.n_species)
+    recv = csr.receivers()
+    g = np.zeros((csr.n_edges, 3))
+    rp = csr.row_ptr.astype(np.int64)
+    for i0, i1 in _blocks(csr.row_ptr):
+        e0, e1 = rp[i0], rp[i1]
+        if e1 == e0:
+            continue
+        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, rc, want_grad=True)
+        ne = e1 - e0
+        R = st["R"].reshape(ne, 4, C)
+        Y = st["Y"]
+        hj = h[species[csr.col[e0:e1]]]
+        Ab = Abar[recv[e0:e1]]  # [ne, 16, C]
+        rho = R * hj[:, None, :]
+        Ybar = (Ab * rho[:, LIDX, :]).sum(axis=2)  # dE/dY [ne, 16]
+        Rbar = np.zeros((ne, 4, C))
+        for l in range(4):
+            ks = np.flatnonzero(LIDX == l)
+            Rbar[:, l, :] = hj * (Ab[:, ks, :] * Y[:, ks, None]).sum(axis=1)
+        Rbar = Rbar.reshape(ne, 4 * C)
+        bbar = np.zeros((ne, N_BASIS))
+        pp = pairs[e0:e1]
+        for p in np.unique(pp):
+            sel = pp == p
+            s2bar = Rbar[sel] @ _f64(model.W3[p]).T
+            z2bar = s2bar * silu_d(st["z2"][sel])
+            s1bar = z2bar @ _f64(model.W2[p]).T
+            z1bar = s1bar * silu_d(st["z1"][sel])
+            bbar[sel] = z1bar @ _f64(model.W1[p]).T
+        rbar = (bbar * st["db"]).sum(axis=1)
+        G = np.einsum("ek,ekx->ex", Ybar, st["dY"])
+        u = st["u"]
+        r = st["r"]
+        g[e0:e1] = rbar[:, None] * u + (G - (G * u).sum(axis=1, keepdims=True) * u) / r[:, None]
+    return g
+
+
+def forces_from_g(g, csr: CSR):
+    """F_i = sum_{e in row i} (g_e - g_rev(e))  (d_e = x_j - x_i + n L)."""
+    n = len(csr.row_ptr) - 1
+    per_edge = g - g[csr.rev]
+    F = np.zeros((n, 3))
+    recv = csr.receivers()
+    np.add.at(F, recv, per_edge)
+    return F
+
+
+def virial_from_g(d, g):
+    """W_ab = -sum_e d_{e,a} g_{e,b}: the derivative of E under a homogeneous
+    strain x -> (I + eps) x of positions and box is dE/deps_ab = sum_e g_{e,a} d_{e,b},
+    and the virial is its negative (symmetric for a rotation-invariant E)."""
+    return -(d.T @ g)
+
+
+def energy_forces(pos, species, box, model, csr: CSR | None = None, want_virial: bool = False):
+    """The full call: neighbours (if not given), energy, per-atom energy, forces."""
+    pos = np.asarray(pos, np.float64)
+    box = np.asarray(box, np.float64)
+    if csr is None:
+        csr = neighbors_celllist(pos, box, model.cutoff)
+    d = edge_vectors(pos, box, csr)
+    fw = forward_edges(d, csr, species, model)
+    g = backward_edges(d, csr, species, model, fw["A"])
+    out = dict(E=fw["E"], Ei=fw["Ei"], A=fw["A"], g=g, F=forces_from_g(g, csr), csr=csr, d=d)
+    if want_virial:
+        out["virial"] = virial_from_g(d, g)
+    return out
+
+
+def energy_fixed_csr(pos, species, box, model, csr: CSR) -> float:
+    """E as a function of positions with the edge list held fixed (for finite differences)."""
+    d = edge_vectors(pos, box, csr)
+    return forward_edges(d, csr, species, model)["E"]
+
+
+# ------------------------------------------- folded / reassociated last layer
+def message_h_folded(d, csr: CSR, species, model):
+    """A with h folded into the last layer: W3'[k, lC+c] = W3[k, lC+c] h_{Z_j,c}
+    ("deepmd-kit PR #6108", What: a frozen product of two linear maps can be
+    precomputed once)."""
+    C = model.channels
+    S = model.n_species
+    n = len(csr.row_ptr) - 1
+    pairs = pair_index(species, csr, S)
+    recv = csr.receivers()
+    h = _f64(model.emb)
+    A = np.zeros((n, 16, C))
+    rp = csr.row_ptr.astype(np.int64)
+    for i0, i1 in _blocks(csr.row_ptr):
+        e0, e1 = rp[i0], rp[i1]
+        if e1 == e0:
+            continue
+        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, model.cutoff)
+        Rf = np.zeros((e1 - e0, 4 * C))
+        for p in np.unique(pairs[e0:e1]):
+            sel = pairs[e0:e1] == p
+            W3f = _f64(model.W3[p]) * np.tile(h[p % S], 4)[None, :]
+            Rf[sel] = st["s2"][sel] @ W3f
+        Rf = Rf.reshape(-1, 4, C)
+        msg = Rf[:, LIDX, :] * st["Y"][:, :, None]
+        A[i0:i1] = _segment_sum(msg, recv[e0:e1] - i0, i1 - i0)
+    return A
+
+
+def message_reassociated(d, csr: CSR, species, model):
+    """A with the linear last layer moved past the edge sum:
+    T_{i,s,lm,k} = sum_{e in row i, Z_j = s} Y_{e,lm} s2_{e,k},
+    A_{i,lm,c} = sum_s h_{s,c} sum_k W3^{(Z_i,s)}[k, lC+c] T_{i,s,lm,k}."""
+    C = model.channels
+    S = model.n_species
+    n = len(csr.row_ptr) - 1
+    pairs = pair_index(species, csr, S)
+    recv = csr.receivers()
+    h = _f64(model.emb)
+    T = np.zeros((n, S, 16, 64))
+    rp = csr.row_ptr.astype(np.int64)
+    for i0, i1 in _blocks(csr.row_ptr):
+        e0, e1 = rp[i0], rp[i1]
+        if e1 == e0:
+            continue
+        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, model.cutoff)
+        outer = st["Y"][:, :, None] * st["s2"][:, None, :]  # [ne, 16, 64]
+        sj = species[csr.col[e0:e1]]
+        for s in range(S):
+            sel = sj == s
+            if not np.any(sel):
+                continue
+            T[i0:i1, s] += _segment_sum(outer[sel], recv[e0:e1][sel] - i0, i1 - i0)
+    A = np.zeros((n, 16, C))
+    for i in range(n):
+        zi = species[i]
+        for s in range(S):
+            W3 = _f64(model.W3[zi * S + s]).reshape(64, 4, C)  # [k, l, c]
+            # A[lm, c] += h[s, c] * sum_k W3[k, l(lm), c] * T[lm, k]
+            A[i] += h[s][None, :] * np.einsum("mk,kmc->mc", T[i, s], W3[:, LIDX, :])
+    return A
+
+
+def backward_reassociated_terms(d, csr: CSR, species, model, A):
+    """Ybar and s2bar per edge through the per-atom matrix
+    M_{i,s}[lm, k] = sum_c Abar_{i,lm,c} h_{s,c} W3^{(Z_i,s)}[k, lC+c]:
+    Ybar_{e,lm} = sum_k M[lm, k] s2_{e,k},  s2bar_{e,k} = sum_lm M[lm, k] Y_{e,lm}."""
+    C = model.channels
+    S = model.n_species
+    n = len(csr.row_ptr) - 1
+    h = _f64(model.emb)
+    Abar = 2.0 * _f64(model.w_read)[None, None, :] * A
+    M = np.zeros((n, S, 16, 64))
+    for i in range(n):
+        zi = species[i]
+        for s in range(S):
+            W3 = _f64(model.W3[zi * S + s]).reshape(64, 4, C)
+            M[i, s] = np.einsum("mc,kmc->mk", Abar[i] * h[s][None, :], W3[:, LIDX, :])
+    pairs = pair_index(species, csr, S)
+    st = _edge_stage(d, pairs, model, model.cutoff)
+    recv = csr.receivers()
+    Me = M[recv, species[csr.col]]  # [E, 16, 64]
+    Ybar = np.einsum("emk,ek->em", Me, st["s2"])
+    s2bar = np.einsum("emk,em->ek", Me, st["Y"])
+    return Ybar, s2bar
+
+
+def backward_direct_terms(d, csr: CSR, species, model, A):
+    """Ybar and s2bar per edge by the direct chain (for comparison with the
+    reassociated form)."""
+    C = model.channels
+    S = model.n_species
+    h = _f64(model.emb)
+    Abar = 2.0 * _f64(model.w_read)[None, None, :] * A
+    pairs = pair_index(species, csr, S)
+    st = _edge_stage(d, pairs, model, model.cutoff)
+    recv = csr.receivers()
+    ne = csr.n_edges
+    R = st["R"].reshape(ne, 4, C)
+    hj = h[species[csr.col]]
+    Ab = Abar[recv]
+    Ybar = (Ab * (R * hj[:, None, :])[:, LIDX, :]).sum(axis=2)
+    Rbar = np.zeros((ne, 4, C))
+    for l in range(4):
+        ks = np.flatnonzero(LIDX == l)
+        Rbar[:, l, :] = hj * (Ab[:, ks, :] * st["Y"][:, ks, None]).sum(axis=1)
+    Rbar = Rbar.reshape(ne, 4 * C)
+    s2bar = np.zeros((ne, 64))
+    for p in np.unique(pairs):
+        sel = pairs == p
+        s2bar[sel] = Rbar[sel] @ _f64(model.W3[p]).T
+    return Ybar, s2bar
+
+
+# --------------------------------------------------------- per-stage helpers
+def stage_basis(pos, box, csr: CSR, rc: float):
+    """Per-edge r [E], basis [E, 32], Y [E, 16] (what the materialising
+    basis entry point returns)."""
+    d = edge_vectors(pos, box, csr)
+    r, u = geometry(d)
+    return r, radial_basis(r, rc), sph.real_sph(u)
+
+
+def stage_project(basis, csr: CSR, species, model):
+    """R [E, 4C] from a given basis [E, 32], per ordered species pair."""
+    pairs = pair_index(species, csr, model.n_species)
+    R = np.zeros((len(basis), 4 * model.channels))
+    for p in np.unique(pairs):
+        sel = pairs == p
+        R[sel] = radial_mlp(_f64(basis[sel]), _f64(model.W1[p]), _f64(model.W2[p]), _f64(model.W3[p]))[-1]
+    return R
+
+
+def conditioning(out, model, csr: CSR):
+    """kappa_E = sum_i sum_c |w_c| sum_lm A^2 / |E|;
+    kappa_F = max_i sum_{e in row i}(|g_e| + |g_rev|) / RMS(F)."""
+    A = out["A"]
+    w = np.abs(_f64(model.w_read))
+    kE = float(((A**2).sum(axis=1) @ w).sum() / abs(out["E"]))
+    g = out["g"]
+    gn = np.linalg.norm(g, axis=1)
+    per = gn + gn[csr.rev]
+    recv = csr.receivers()
+    tot = np.zeros(len(csr.row_ptr) - 1)
+    np.add.at(tot, recv, per)
+    rms = float(np.sqrt((out["F"] ** 2).mean()))
+    return kE, float(tot.max() / rms), rms
