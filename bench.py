@@ -1,0 +1,165 @@
+#!/usr/bin/env python3
+"""Throughput of one energy + force call (forward + force backward, FP32) on
+one MI355X, in edges per second.
+
+Default workload: the 4096-atom carbon diamond (8 x 8 x 8 conventional cells,
+a = 3.567 A, 0.02 A seeded noise, cutoff 6.0 A, E = 647,168 directed edges),
+one species, 64 channels.  Inputs are synthetic and seeded (eec_inputs); the
+neighbour list is built once before timing (it is timed separately and
+reported as context).  Each timed step is one full eec_energy_forces call:
+radial network + streamed message + readout + streaming backward + force
+scatter, with every input already resident in device memory.
+
+Also reported:
+  roofline      the dominant kernel (the streaming backward), its launch
+                duration measured with hipEvents recorded by the library on
+                the stream it launches on; algorithmic flops per edge
+                (network input gradient 45,056 + Rbar 2,304 + Ybar 2,048)
+                over that duration, against the FP32 matrix peak;
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload
+                (the first 1024 receivers: their forward and force backward),
+                on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edges/s fwd+force bwd, fp32, 4096-atom diamond (E≈6.5e5); % of roofline"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+# algorithmic flops per edge of the backward kernel (recomputation excluded)
+BWD_FLOP_PER_EDGE = 45056 + 2304 + 2048
+FWD_FLOP_PER_EDGE = 45056 + 2304
+WORKLOADS = {
+    "D4096": "diamond 8x8x8 conventional cells, 4096 atoms, a=3.567 A, rc=6.0 A, 0.02 A noise, seed 0, C=64",
+    "D512": "diamond 4x4x4 conventional cells, 512 atoms, rc=6.0 A, C=64",
+    "D64": "diamond 2x2x2 conventional cells, 64 atoms, rc=6.0 A, C=64",
+    "RS": "rocksalt 8x8x8 cells, 4096 atoms, 2 species, a=5.64 A, rc=6.0 A, C=64",
+    "PV": "cubic perovskite 10x10x10 cells, 5000 atoms, 3 species, a=3.95 A, rc=6.0 A, C=64",
+    "D32k": "diamond 16x16x16 conventional cells, 32768 atoms, rc=6.0 A, C=128",
+}
+
+
+def cpu_baseline(cfg, n_rows: int = 1024):
+    """The oracle (as it stands) on the first n_rows receivers of the workload."""
+    import numpy as np
+
+    from oracle import model as M
+    from oracle import neighbors as N
+
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    rp = csr.row_ptr.astype(np.int64)
+    n_rows = min(n_rows, cfg.n_atoms)
+    e1 = int(rp[n_rows])
+    recv = csr.receivers()[:e1]
+    edges = np.arange(e1)
+    d = (cfg.pos[csr.col[edges]] - cfg.pos[recv]) + csr.shift[edges].astype(np.float64) * cfg.box[None, :]
+    pairs = cfg.species[recv].astype(np.int64) * cfg.model.n_species + cfg.species[csr.col[edges]]
+    h = np.asarray(cfg.model.emb, np.float64)
+    hj = h[cfg.species[csr.col[edges]]]
+    w = np.asarray(cfg.model.w_read, np.float64)
+    t0 = time.perf_counter()
+    msg, _ = M.edge_messages(d, pairs, hj, cfg.model)
+    A = np.zeros((n_rows, 16, cfg.model.channels))
+    np.add.at(A, recv, msg)
+    Abar = 2.0 * w[None, None, :] * A
+    M.edge_backward(d, pairs, hj, Abar[recv], cfg.model)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": e1 / dt, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_rows} receivers of the workload ({e1} edges): float64 forward "
+                      f"(basis, network, harmonics, message) and force backward; {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the single-GPU figure is the workload's throughput)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import eec_inputs as I
+    from equivariant_edge_convolution_amd import binding as B
+
+    dev = torch.device("cuda:0")
+    cfg = I.make_config(args.config)
+    pos = torch.as_tensor(cfg.pos).to(dev)
+    species = torch.as_tensor(cfg.species).to(dev)
+    model = B.Model.from_arrays(cfg.model, dev)
+
+    # neighbour list (context; not in the timed step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g = B.build_neighbors(pos, cfg.box, cfg.model.cutoff, species, cfg.model.n_species)
+    torch.cuda.synchronize()
+    nb_ms = (time.perf_counter() - t0) * 1e3
+    E = g.n_edges
+
+    ef = B.EnergyForces(g, model, dev, atom_energy=True)
+    nph = len(B.PHASES)
+    ev = B.HipEvents(2 * nph * max(args.steps, 1))
+    for _ in range(args.warmup):
+        ef(pos, cfg.box, species)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ef(pos, cfg.box, species, events=ev.handles[2 * nph * k: 2 * nph * (k + 1)])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    phase_ms = {}
+    for p, name in enumerate(B.PHASES):
+        phase_ms[name] = float(np.mean([ev.elapsed_ms(2 * nph * k + 2 * p, 2 * nph * k + 2 * p + 1)
+                                        for k in range(args.steps)]))
+    ev.close()
+    energy = float(ef.energy.cpu()[0])
+
+    bwd_ms = phase_ms["backward"]
+    achieved = BWD_FLOP_PER_EDGE * E / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": E / (ms_per_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "n_atoms": cfg.n_atoms,
+                   "n_edges": E, "channels": cfg.model.channels, "n_species": cfg.model.n_species},
+        "roofline": {"bound": "mfma", "kernel": "k_backward", "achieved": achieved,
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "flop_per_edge": BWD_FLOP_PER_EDGE, "launch_ms": bwd_ms},
+        "phases_ms": phase_ms,
+        "neighbors_ms": nb_ms,
+        "energy": energy,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -71,6 +71,7 @@ CONFIGS = {
     "PV2": ("perovskite", 2, 64),
     "PV3": ("perovskite", 3, 64),
     "D64c128": ("diamond", 2, 128),
+    "D512c128": ("diamond", 4, 128),
 }
 
 

@@ -1,0 +1,302 @@
+// C ABI of the edge-convolution library: argument checks, workspace layout and
+// the launch sequence of each entry point on the caller's stream.
+#include <math.h>
+
+#include <algorithm>
+#include <initializer_list>
+#include <string>
+
+#include "eec_device.hpp"
+#include "eec_internal.hpp"
+
+using namespace eec;
+
+namespace {
+
+thread_local std::string g_err;
+
+eec_status fail(eec_status st, const std::string& why) {
+  g_err = why;
+  return st;
+}
+eec_status ok() {
+  g_err.clear();
+  return EEC_OK;
+}
+
+struct Span {
+  uintptr_t a = 0, b = 0;
+  const char* name = "";
+};
+Span span(const void* p, size_t bytes, const char* name) {
+  Span s;
+  s.a = (uintptr_t)p;
+  s.b = s.a + bytes;
+  s.name = name;
+  if (p == nullptr || bytes == 0) s.b = s.a;
+  return s;
+}
+bool overlap(const Span& x, const Span& y) { return x.a < y.b && y.a < x.b; }
+
+// Every output must be disjoint from every input and from the other outputs.
+eec_status check_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (auto i = ins.begin(); i != ins.end(); ++i)
+      if (overlap(*o, *i)) return fail(EEC_ERR_ALIAS, std::string(o->name) + " overlaps input " + i->name);
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return fail(EEC_ERR_ALIAS, std::string(o->name) + " overlaps " + o2->name);
+  }
+  return EEC_OK;
+}
+
+eec_status check_box(const double* box, double cutoff) {
+  if (box == nullptr) return fail(EEC_ERR_NULL, "box is NULL");
+  if (!(isfinite(cutoff) && cutoff > 0.0)) return fail(EEC_ERR_SHAPE, "cutoff must be finite and > 0");
+  for (int k = 0; k < 3; ++k)
+    if (!(isfinite(box[k]) && box[k] > 0.0 && box[k] >= cutoff))
+      return fail(EEC_ERR_BOX, "every box side must be finite, > 0 and >= cutoff");
+  return EEC_OK;
+}
+
+eec_status check_model(const eec_model* m) {
+  if (m == nullptr) return fail(EEC_ERR_NULL, "model is NULL");
+  if (!m->W1 || !m->W2 || !m->W3 || !m->emb || !m->w_read) return fail(EEC_ERR_NULL, "a model weight pointer is NULL");
+  if (m->n_basis != NB || m->hidden != HID || m->lmax != 3)
+    return fail(EEC_ERR_SHAPE, "model must have n_basis 32, hidden 64, lmax 3");
+  if (m->channels != 64 && m->channels != 128) return fail(EEC_ERR_SHAPE, "channels must be 64 or 128");
+  if (m->n_species < 1 || m->n_species > 4) return fail(EEC_ERR_SHAPE, "n_species must be in [1, 4]");
+  if (!(isfinite(m->cutoff) && m->cutoff > 0.0)) return fail(EEC_ERR_SHAPE, "model cutoff must be finite and > 0");
+  if (((uintptr_t)m->emb & 15) != 0) return fail(EEC_ERR_SHAPE, "emb must be 16-byte aligned");
+  return EEC_OK;
+}
+
+eec_status check_graph(const eec_graph* g) {
+  if (g == nullptr || g->row_ptr == nullptr) return fail(EEC_ERR_NULL, "graph or row_ptr is NULL");
+  if (g->n_atoms < 0 || g->n_edges < 0 || g->n_edges > INT32_MAX) return fail(EEC_ERR_SHAPE, "bad graph sizes");
+  if (g->n_edges > 0 && (!g->col || !g->shift || !g->rev)) return fail(EEC_ERR_NULL, "graph edge arrays are NULL");
+  if (g->n_edges > 0 && g->n_atoms == 0) return fail(EEC_ERR_SHAPE, "edges without atoms");
+  return EEC_OK;
+}
+
+eec_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return EEC_OK;
+  if (ws == nullptr) return fail(EEC_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws & 255) != 0) return fail(EEC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(EEC_ERR_WORKSPACE, "workspace is smaller than required");
+  return EEC_OK;
+}
+
+eec_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(EEC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+#define TRY(x)                      \
+  do {                              \
+    eec_status st_ = (x);           \
+    if (st_ != EEC_OK) return st_;  \
+  } while (0)
+
+Span graph_span_rp(const eec_graph* g) { return span(g->row_ptr, 4 * (size_t)(g->n_atoms + 1), "row_ptr"); }
+Span graph_span_col(const eec_graph* g) { return span(g->col, 4 * (size_t)g->n_edges, "col"); }
+Span graph_span_shift(const eec_graph* g) { return span(g->shift, 3 * (size_t)g->n_edges, "shift"); }
+Span graph_span_rev(const eec_graph* g) { return span(g->rev, 4 * (size_t)g->n_edges, "rev"); }
+
+Span model_span(const float* p, const eec_model* m, int which) {
+  const size_t P = (size_t)m->n_species * m->n_species, C = m->channels;
+  switch (which) {
+    case 1: return span(p, 4 * P * NB * HID, "W1");
+    case 2: return span(p, 4 * P * HID * HID, "W2");
+    case 3: return span(p, 4 * P * HID * 4 * C, "W3");
+    case 4: return span(p, 4 * (size_t)m->n_species * C, "emb");
+    default: return span(p, 4 * C, "w_read");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* eec_last_error(void) { return g_err.c_str(); }
+
+size_t eec_neighbors_workspace_bytes(int32_t n_atoms, const double* box, double cutoff) {
+  if (box == nullptr || n_atoms < 0 || !(cutoff > 0.0)) return 0;
+  return nb_plan(n_atoms, box, cutoff).bytes;
+}
+
+eec_status eec_build_neighbors(void* stream, int32_t n_atoms, const double* pos, const double* box,
+                               double cutoff, const int32_t* species, int32_t n_species,
+                               int64_t edge_capacity, int32_t* row_ptr, int32_t* col, int8_t* shift,
+                               int32_t* rev, int64_t* n_edges, void* workspace,
+                               size_t workspace_bytes) {
+  if (n_edges == nullptr || row_ptr == nullptr) return fail(EEC_ERR_NULL, "n_edges or row_ptr is NULL");
+  if (n_atoms < 0 || edge_capacity < 0) return fail(EEC_ERR_SHAPE, "negative size");
+  if (n_atoms > 0 && pos == nullptr) return fail(EEC_ERR_NULL, "pos is NULL");
+  if (species != nullptr && n_species < 1) return fail(EEC_ERR_SHAPE, "n_species must be >= 1");
+  if (edge_capacity > 0 && (!col || !shift || !rev)) return fail(EEC_ERR_NULL, "CSR arrays are NULL");
+  TRY(check_box(box, cutoff));
+  const NbPlan p = nb_plan(n_atoms, box, cutoff);
+  TRY(check_ws(workspace, workspace_bytes, p.bytes));
+  const size_t cap = (size_t)edge_capacity;
+  TRY(check_alias({span(row_ptr, 4 * (size_t)(n_atoms + 1), "row_ptr"), span(col, 4 * cap, "col"),
+                   span(shift, 3 * cap, "shift"), span(rev, 4 * cap, "rev"),
+                   span(workspace, workspace_bytes, "workspace")},
+                  {span(pos, 24 * (size_t)n_atoms, "pos"), span(species, 4 * (size_t)n_atoms, "species")}));
+  const char* why = "";
+  const eec_status st = nb_build((hipStream_t)stream, p, n_atoms, pos, box, cutoff, species, n_species,
+                                 edge_capacity, row_ptr, col, shift, rev, n_edges, (char*)workspace, &why);
+  if (st != EEC_OK) return fail(st, why);
+  return launched("build_neighbors");
+}
+
+eec_status eec_radial_basis(void* stream, const eec_graph* g, const double* pos, const double* box,
+                            double cutoff, float* r, float* basis, float* Y) {
+  TRY(check_graph(g));
+  TRY(check_box(box, cutoff));
+  if (g->n_atoms > 0 && pos == nullptr) return fail(EEC_ERR_NULL, "pos is NULL");
+  const size_t E = (size_t)g->n_edges;
+  TRY(check_alias({span(r, 4 * E, "r"), span(basis, 4 * E * NB, "basis"), span(Y, 4 * E * NLM, "Y")},
+                  {span(pos, 24 * (size_t)g->n_atoms, "pos"), graph_span_rp(g), graph_span_col(g),
+                   graph_span_shift(g), graph_span_rev(g)}));
+  Box b{{box[0], box[1], box[2]}};
+  launch_basis((hipStream_t)stream, g, pos, b, cutoff, r, basis, Y);
+  return launched("radial_basis");
+}
+
+size_t eec_project_workspace_bytes(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
+  if (m == nullptr || n_atoms < 0 || n_edges < 0) return 0;
+  return conv_plan(n_atoms, n_edges, m).off_A;
+}
+
+eec_status eec_radial_project(void* stream, const eec_graph* g, const int32_t* species,
+                              const eec_model* m, const float* basis, float* R, void* workspace,
+                              size_t workspace_bytes) {
+  TRY(check_graph(g));
+  TRY(check_model(m));
+  if (g->n_edges > 0 && (!species || !basis || !R)) return fail(EEC_ERR_NULL, "species, basis or R is NULL");
+  const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
+  TRY(check_ws(workspace, workspace_bytes, p.off_A));
+  const size_t E = (size_t)g->n_edges, NC = 4 * (size_t)m->channels;
+  TRY(check_alias({span(R, 4 * E * NC, "R"), span(workspace, workspace_bytes, "workspace")},
+                  {span(basis, 4 * E * NB, "basis"), span(species, 4 * (size_t)g->n_atoms, "species"),
+                   graph_span_rp(g), graph_span_col(g), graph_span_shift(g), graph_span_rev(g),
+                   model_span(m->W1, m, 1), model_span(m->W2, m, 2), model_span(m->W3, m, 3),
+                   model_span(m->emb, m, 4), model_span(m->w_read, m, 5)}));
+  if (E == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  launch_prepare(s, p, g, species, ws, nullptr);
+  Box b{{1.0, 1.0, 1.0}};
+  launch_radial(s, p, g, nullptr, b, m->cutoff, species, m, basis, 0, p.E, R, nullptr, ws);
+  return launched("radial_project");
+}
+
+size_t eec_workspace_bytes(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
+  if (m == nullptr || n_atoms < 0 || n_edges < 0) return 0;
+  return conv_plan(n_atoms, n_edges, m).bytes;
+}
+
+static eec_status forward_common(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                                 const double* box, const int32_t* species, const eec_model* m, float* A,
+                                 char* ws) {
+  launch_prepare(s, p, g, species, ws, A);
+  Box b{{box[0], box[1], box[2]}};
+  float* Rc = (float*)(ws + p.off_R);
+  float* Yc = (float*)(ws + p.off_Y);
+  for (int64_t e0 = 0; e0 < p.E; e0 += p.chunk) {
+    const int64_t e1 = std::min<int64_t>(p.E, e0 + p.chunk);
+    launch_radial(s, p, g, pos, b, m->cutoff, species, m, nullptr, e0, e1, Rc, Yc, ws);
+    launch_message(s, p, g, species, m, e0, e1, Rc, Yc, A, ws);
+  }
+  return EEC_OK;
+}
+
+eec_status eec_edge_message(void* stream, const eec_graph* g, const double* pos, const double* box,
+                            const int32_t* species, const eec_model* m, float* A, void* workspace,
+                            size_t workspace_bytes) {
+  TRY(check_graph(g));
+  TRY(check_model(m));
+  TRY(check_box(box, m->cutoff));
+  if (g->n_atoms > 0 && (!pos || !species || !A)) return fail(EEC_ERR_NULL, "pos, species or A is NULL");
+  const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
+  TRY(check_ws(workspace, workspace_bytes, p.bytes));
+  const size_t N = (size_t)g->n_atoms;
+  TRY(check_alias({span(A, 4 * N * NLM * m->channels, "A"), span(workspace, workspace_bytes, "workspace")},
+                  {span(pos, 24 * N, "pos"), span(species, 4 * N, "species"), graph_span_rp(g),
+                   graph_span_col(g), graph_span_shift(g), graph_span_rev(g), model_span(m->W1, m, 1),
+                   model_span(m->W2, m, 2), model_span(m->W3, m, 3), model_span(m->emb, m, 4),
+                   model_span(m->w_read, m, 5)}));
+  if (N == 0) return ok();
+  forward_common((hipStream_t)stream, p, g, pos, box, species, m, A, (char*)workspace);
+  return launched("edge_message");
+}
+
+static eec_status energy_forces_impl(void* stream, const eec_graph* g, const double* pos,
+                                     const double* box, const int32_t* species, const eec_model* m,
+                                     float* energy, float* atom_energy, float* forces, float* virial,
+                                     void* workspace, size_t workspace_bytes, void* const* events) {
+  TRY(check_graph(g));
+  TRY(check_model(m));
+  TRY(check_box(box, m->cutoff));
+  if (energy == nullptr) return fail(EEC_ERR_NULL, "energy is NULL");
+  if (g->n_atoms > 0 && (!pos || !species || !forces)) return fail(EEC_ERR_NULL, "pos, species or forces is NULL");
+  const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
+  TRY(check_ws(workspace, workspace_bytes, p.bytes));
+  const size_t N = (size_t)g->n_atoms;
+  TRY(check_alias({span(energy, 4, "energy"), span(atom_energy, 4 * N, "atom_energy"),
+                   span(forces, 12 * N, "forces"), span(virial, 36, "virial"),
+                   span(workspace, workspace_bytes, "workspace")},
+                  {span(pos, 24 * N, "pos"), span(species, 4 * N, "species"), graph_span_rp(g),
+                   graph_span_col(g), graph_span_shift(g), graph_span_rev(g), model_span(m->W1, m, 1),
+                   model_span(m->W2, m, 2), model_span(m->W3, m, 3), model_span(m->emb, m, 4),
+                   model_span(m->w_read, m, 5)}));
+  hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int k) {
+    if (events != nullptr) hipEventRecord((hipEvent_t)events[k], s);
+  };
+  char* ws = (char*)workspace;
+  float* A = (float*)(ws + p.off_A);
+  float* ei = atom_energy ? atom_energy : (float*)(ws + p.off_ei);
+  Box b{{box[0], box[1], box[2]}};
+  float* Rc = (float*)(ws + p.off_R);
+  float* Yc = (float*)(ws + p.off_Y);
+  mark(2 * EEC_PHASE_PREPARE);
+  launch_prepare(s, p, g, species, ws, A);
+  mark(2 * EEC_PHASE_PREPARE + 1);
+  mark(2 * EEC_PHASE_FORWARD);
+  for (int64_t e0 = 0; e0 < p.E; e0 += p.chunk) {
+    const int64_t e1 = std::min<int64_t>(p.E, e0 + p.chunk);
+    launch_radial(s, p, g, pos, b, m->cutoff, species, m, nullptr, e0, e1, Rc, Yc, ws);
+    launch_message(s, p, g, species, m, e0, e1, Rc, Yc, A, ws);
+  }
+  mark(2 * EEC_PHASE_FORWARD + 1);
+  mark(2 * EEC_PHASE_READOUT);
+  launch_readout(s, p, m, A, ei, nullptr, energy);  // A now holds dE/dA
+  mark(2 * EEC_PHASE_READOUT + 1);
+  float* gbuf = (float*)(ws + p.off_g);
+  mark(2 * EEC_PHASE_BACKWARD);
+  launch_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);
+  mark(2 * EEC_PHASE_BACKWARD + 1);
+  mark(2 * EEC_PHASE_SCATTER);
+  launch_scatter(s, p, g, pos, b, gbuf, forces, (double*)(ws + p.off_vpart), virial);
+  mark(2 * EEC_PHASE_SCATTER + 1);
+  return launched("energy_forces");
+}
+
+eec_status eec_energy_forces(void* stream, const eec_graph* g, const double* pos, const double* box,
+                             const int32_t* species, const eec_model* m, float* energy, float* atom_energy,
+                             float* forces, float* virial, void* workspace, size_t workspace_bytes) {
+  return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
+                            workspace_bytes, nullptr);
+}
+
+eec_status eec_energy_forces_timed(void* stream, const eec_graph* g, const double* pos, const double* box,
+                                   const int32_t* species, const eec_model* m, float* energy,
+                                   float* atom_energy, float* forces, float* virial, void* workspace,
+                                   size_t workspace_bytes, void* const* events) {
+  return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
+                            workspace_bytes, events);
+}
+
+}  // extern "C"

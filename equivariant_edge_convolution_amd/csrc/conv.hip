@@ -1,0 +1,474 @@
+// Memory-bound kernels of the edge convolution: graph preparation, the
+// streaming message and receiver reduction, the energy readout, the force
+// scatter (with virial) and the materialised basis.
+//
+// Every per-atom sum runs in a fixed order with no float atomics: the pages
+// reject a per-atom reduction that needs atomics because it breaks
+// reproducible gradients ("FastMACE rewrite screens", OPT-T02 stage D) and keep
+// deterministic graph sums (OPT4-T02 polar_graph_sums).
+#include <algorithm>
+
+#include "eec_device.hpp"
+#include "eec_internal.hpp"
+
+namespace eec {
+namespace {
+
+inline int blocks_for(int64_t n, int per) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>((n + per - 1) / per, 1 << 20));
+}
+
+// ------------------------------------------------------------ preparation
+// recv[e] = receiver of edge e; zero A rows of atoms without edges.
+__global__ void __launch_bounds__(256) k_recv(int32_t n, const int32_t* __restrict__ rp,
+                                              int64_t E, int32_t* __restrict__ recv,
+                                              float* __restrict__ A, int C) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const int a = max(0, min(rp[i], (int)E)), b = max(a, min(rp[i + 1], (int)E));
+  for (int e = a + lane; e < b; e += 64) recv[e] = i;
+  if (A != nullptr && a == b)
+    for (int k = lane; k < NLM * C; k += 64) A[(size_t)i * NLM * C + k] = 0.f;
+}
+
+constexpr int PB = 1024;  // edges per counting block
+
+__device__ __forceinline__ int pair_of(int64_t e, const int32_t* recv, const int32_t* col,
+                                       const int32_t* species, int S, int n) {
+  const int i = min(max(recv[e], 0), n - 1), j = min(max(col[e], 0), n - 1);
+  const int zi = min(max(species[i], 0), S - 1), zj = min(max(species[j], 0), S - 1);
+  return zi * S + zj;
+}
+
+__global__ void __launch_bounds__(256) k_pair_count(int64_t E, const int32_t* __restrict__ recv,
+                                                    const int32_t* __restrict__ col,
+                                                    const int32_t* __restrict__ species, int S,
+                                                    int n, int64_t nb, int32_t* __restrict__ cnt) {
+  __shared__ int32_t c[16];
+  const int P = S * S;
+  if (threadIdx.x < 16) c[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t b = blockIdx.x;
+  for (int k = threadIdx.x; k < PB; k += blockDim.x) {
+    const int64_t e = b * PB + k;
+    if (e < E) atomicAdd(&c[pair_of(e, recv, col, species, S, n)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < P) cnt[(int64_t)threadIdx.x * nb + b] = c[threadIdx.x];
+}
+
+// Exclusive scan (pair-major, then block) of the block counts; pair_start[p].
+__global__ void __launch_bounds__(1024) k_pair_scan(int64_t nb, int P, const int32_t* __restrict__ cnt,
+                                                    int64_t* __restrict__ off,
+                                                    int64_t* __restrict__ pair_start, int64_t E) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t n = nb * P;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = std::min<int64_t>(n, t * per), b = std::min<int64_t>(n, a + per);
+  int64_t s = 0;
+  for (int64_t k = a; k < b; ++k) s += cnt[k];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int64_t v = (t >= o) ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = part[t] - s;
+  for (int64_t k = a; k < b; ++k) {
+    off[k] = run;
+    if (k % nb == 0) pair_start[k / nb] = run;
+    run += cnt[k];
+  }
+  if (t == 0) pair_start[P] = E;
+}
+
+// Stable scatter: perm[pos] = e with edges grouped by pair, CSR order inside a group.
+__global__ void __launch_bounds__(256) k_pair_scatter(int64_t E, const int32_t* __restrict__ recv,
+                                                      const int32_t* __restrict__ col,
+                                                      const int32_t* __restrict__ species, int S,
+                                                      int n, int64_t nb,
+                                                      const int64_t* __restrict__ off,
+                                                      int32_t* __restrict__ perm) {
+  __shared__ int32_t pre[16][257];
+  const int P = S * S;
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  int pr[4];
+  int mycnt[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) mycnt[p] = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t e = b * PB + 4 * t + k;
+    pr[k] = (e < E) ? pair_of(e, recv, col, species, S, n) : -1;
+    if (pr[k] >= 0) mycnt[pr[k]]++;
+  }
+  for (int p = 0; p < P; ++p) pre[p][t + 1] = mycnt[p];
+  if (t == 0)
+    for (int p = 0; p < P; ++p) pre[p][0] = 0;
+  __syncthreads();
+  // inclusive scan over threads per pair (Hillis-Steele on entries 1..256)
+  for (int o = 1; o < 256; o <<= 1) {
+    int v[16];
+    for (int p = 0; p < P; ++p) v[p] = (t >= o) ? pre[p][t + 1 - o] : 0;
+    __syncthreads();
+    for (int p = 0; p < P; ++p) pre[p][t + 1] += v[p];
+    __syncthreads();
+  }
+  int seen[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) seen[p] = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int p = pr[k];
+    if (p < 0) continue;
+    const int64_t e = b * PB + 4 * t + k;
+    const int64_t pos = off[(int64_t)p * nb + b] + pre[p][t] + seen[p];
+    seen[p]++;
+    perm[pos] = (int32_t)e;
+  }
+}
+
+// ------------------------------------------------------------ message
+// One workgroup of 4 waves per receiver; lanes over channels; each wave sums a
+// contiguous quarter of the receiver's edges inside the chunk in CSR order, and
+// the quarters are added in a fixed order.
+template <int C>
+__global__ void __launch_bounds__(256) k_message(int64_t e0, int64_t e1, const int32_t* __restrict__ rp,
+                                                 const int32_t* __restrict__ recv,
+                                                 const int32_t* __restrict__ col,
+                                                 const int32_t* __restrict__ species,
+                                                 const float* __restrict__ emb, int S, int n,
+                                                 const float* __restrict__ Rc,
+                                                 const float* __restrict__ Yc, float* __restrict__ A) {
+  constexpr int CPL = C / 64;  // channels per lane
+  constexpr int NC = 4 * C;
+  __shared__ float part[3][NLM * C];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i_first = recv[e0], i_last = recv[e1 - 1];
+  for (int i = i_first + blockIdx.x; i <= i_last; i += gridDim.x) {
+    const int64_t ra = std::max<int64_t>(rp[i], e0), rb = std::min<int64_t>(rp[i + 1], e1);
+    const int64_t len = rb - ra, per = (len + 3) / 4;
+    const int64_t wa = std::min(rb, ra + wave * per), wb = std::min(rb, wa + per);
+    float acc[CPL][NLM];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
+    for (int64_t e = wa; e < wb; ++e) {
+      const int64_t el = __builtin_amdgcn_readfirstlane((int)(e - e0));
+      const int j = min(max(col[e0 + el], 0), n - 1);
+      const int zj = min(max(species[j], 0), S - 1);
+      const float* yr = Yc + el * NLM;
+      const float* rr = Rc + el * NC;
+      float y[NLM];
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) y[k] = yr[k];
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c = lane + 64 * q;
+        const float hc = emb[zj * C + c];
+        const float r0 = rr[c] * hc, r1 = rr[C + c] * hc, r2 = rr[2 * C + c] * hc, r3 = rr[3 * C + c] * hc;
+        acc[q][0] += r0 * y[0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) acc[q][k] += r1 * y[k];
+#pragma unroll
+        for (int k = 4; k < 9; ++k) acc[q][k] += r2 * y[k];
+#pragma unroll
+        for (int k = 9; k < 16; ++k) acc[q][k] += r3 * y[k];
+      }
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < CPL; ++q)
+#pragma unroll
+        for (int k = 0; k < NLM; ++k) part[wave - 1][k * C + lane + 64 * q] = acc[q][k];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const bool assign = rp[i] >= e0;
+      float* ai = A + (size_t)i * NLM * C;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q)
+#pragma unroll
+        for (int k = 0; k < NLM; ++k) {
+          const int idx = k * C + lane + 64 * q;
+          float v = ((acc[q][k] + part[0][idx]) + part[1][idx]) + part[2][idx];
+          ai[idx] = assign ? v : ai[idx] + v;
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ readout
+// One wave per atom: E_i = sum_c w_c sum_lm A^2 (fixed lane order and shuffle
+// tree), Abar = 2 w A written over A.
+template <int C>
+__global__ void __launch_bounds__(256) k_readout(int32_t n, const float* __restrict__ w,
+                                                 float* __restrict__ A, float* __restrict__ ei) {
+  constexpr int CPL = C / 64;
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  float* ai = A + (size_t)i * NLM * C;
+  float sum = 0.f;
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + 64 * q;
+    const float wc = w[c];
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < NLM; ++k) {
+      const float a = ai[k * C + c];
+      s2 += a * a;
+      ai[k * C + c] = 2.f * wc * a;
+    }
+    sum += wc * s2;
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) ei[i] = sum;
+}
+
+// E = sum_i E_i in binary64, one workgroup, contiguous thread slices then a tree.
+__global__ void __launch_bounds__(1024) k_energy_total(int32_t n, const float* __restrict__ ei,
+                                                       float* __restrict__ energy) {
+  __shared__ double part[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = std::min(n, t * per), b = std::min(n, a + per);
+  double s = 0.0;
+  for (int k = a; k < b; ++k) s += (double)ei[k];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (t < o) part[t] += part[t + o];
+    __syncthreads();
+  }
+  if (t == 0) energy[0] = (float)part[0];
+}
+
+// ------------------------------------------------------------ force scatter
+// One wave per atom: F_i = sum_{e in row i} (g_e - g_rev(e)); lanes take a fixed
+// stride of the row, then a fixed shuffle tree.  With `vpart`, also the atom's
+// share of the virial -sum_e d_e g_e^T (in binary64).
+template <bool VIRIAL>
+__global__ void __launch_bounds__(256) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
+                                                 const int32_t* __restrict__ col,
+                                                 const int8_t* __restrict__ shift,
+                                                 const int32_t* __restrict__ rev,
+                                                 const double* __restrict__ pos, double Lx, double Ly,
+                                                 double Lz, const float* __restrict__ g,
+                                                 float* __restrict__ F, double* __restrict__ vpart) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  float fx = 0.f, fy = 0.f, fz = 0.f;
+  double v[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) v[k] = 0.0;
+  const int a = rp[i], b = rp[i + 1];
+  for (int e = a + lane; e < b; e += 64) {
+    const int er = min(max(rev[e], 0), (int)E - 1);
+    const float gx = g[3 * e], gy = g[3 * e + 1], gz = g[3 * e + 2];
+    fx += gx - g[3 * er];
+    fy += gy - g[3 * er + 1];
+    fz += gz - g[3 * er + 2];
+    if (VIRIAL) {
+      const int j = min(max(col[e], 0), n - 1);
+      double d[3];
+      edge_vector(pos, i, j, shift + 3 * e, Lx, Ly, Lz, d);
+      const double gg[3] = {gx, gy, gz};
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) v[3 * p + q] -= d[p] * gg[q];
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    fx += __shfl_xor(fx, off);
+    fy += __shfl_xor(fy, off);
+    fz += __shfl_xor(fz, off);
+    if (VIRIAL)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) v[k] += __shfl_xor(v[k], off);
+  }
+  if (lane == 0) {
+    F[3 * i] = fx;
+    F[3 * i + 1] = fy;
+    F[3 * i + 2] = fz;
+    if (VIRIAL)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) vpart[9 * (size_t)i + k] = v[k];
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_virial_total(int32_t n, const double* __restrict__ vpart,
+                                                       float* __restrict__ virial) {
+  __shared__ double part[9][1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = std::min(n, t * per), b = std::min(n, a + per);
+  double s[9];
+  for (int k = 0; k < 9; ++k) s[k] = 0.0;
+  for (int i = a; i < b; ++i)
+    for (int k = 0; k < 9; ++k) s[k] += vpart[9 * (size_t)i + k];
+  for (int k = 0; k < 9; ++k) part[k][t] = s[k];
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (t < o)
+      for (int k = 0; k < 9; ++k) part[k][t] += part[k][t + o];
+    __syncthreads();
+  }
+  if (t < 9) virial[t] = (float)part[t][0];
+}
+
+// ------------------------------------------------------------ materialised basis
+__global__ void __launch_bounds__(256) k_basis(int64_t E, int32_t n, const int32_t* __restrict__ rp,
+                                               const int32_t* __restrict__ col,
+                                               const int8_t* __restrict__ shift,
+                                               const double* __restrict__ pos, double Lx, double Ly,
+                                               double Lz, double rc, float* __restrict__ r_out,
+                                               float* __restrict__ basis, float* __restrict__ Y) {
+  // two threads per edge: half h computes basis 16 h + 1 .. 16 h + 16
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t e = t >> 1;
+  const int h = (int)(t & 1);
+  if (e >= E) return;
+  // receiver: last row whose start is <= e
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)rp[mid] <= e) lo = mid; else hi = mid;
+  }
+  const int i = lo, j = min(max(col[e], 0), n - 1);
+  double d[3];
+  edge_vector(pos, i, j, shift + 3 * e, Lx, Ly, Lz, d);
+  const double r = sqrt(norm2_nofma(d));
+  if (basis) {
+    float b[16];
+    basis16<false>(r, rc, 16 * h + 1, b, nullptr);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) basis[e * NB + 16 * h + k] = b[k];
+  }
+  if (h == 0) {
+    if (r_out) r_out[e] = (float)r;
+    if (Y) {
+      const double ir = 1.0 / r;
+      float y[16];
+      sph16((float)(d[0] * ir), (float)(d[1] * ir), (float)(d[2] * ir), y);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Y[e * NLM + k] = y[k];
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
+  ConvPlan p{};
+  p.C = m->channels;
+  p.NC = 4 * p.C;
+  p.S = m->n_species;
+  p.P = p.S * p.S;
+  p.E = n_edges;
+  p.N = n_atoms;
+  // Chunk of streamed radial rows: 64 MiB of R, so the chunk the message pass
+  // reads back stays inside the 256 MB last-level cache.
+  const int64_t chunk_rows = (int64_t)(64 << 20) / (4 * p.NC);
+  p.chunk = std::max<int64_t>(1, std::min<int64_t>(n_edges, chunk_rows));
+  p.n_count_blocks = (n_edges + PB - 1) / PB;
+  const int64_t N = std::max(n_atoms, 1), E = std::max<int64_t>(n_edges, 1);
+  size_t o = 0;
+  p.off_recv = o; o += align256(4 * (size_t)E);
+  if (p.S > 1) {
+    p.off_perm = o;       o += align256(4 * (size_t)E);
+    p.off_pair_start = o; o += align256(8 * (size_t)(p.P + 1));
+    p.off_blockcnt = o;   o += align256((4 + 8) * (size_t)p.P * std::max<int64_t>(p.n_count_blocks, 1));
+  }
+  p.off_A = o;     o += align256(4 * (size_t)N * NLM * p.C);
+  p.off_R = o;     o += align256(4 * (size_t)p.chunk * p.NC);
+  p.off_Y = o;     o += align256(4 * (size_t)p.chunk * NLM);
+  p.off_g = o;     o += align256(4 * 3 * (size_t)E);
+  p.off_ei = o;    o += align256(4 * (size_t)N);
+  p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
+  p.off_epart = o; o += 256;
+  p.bytes = o;
+  return p;
+}
+
+void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
+                    char* ws, float* zero_rows_of) {
+  int32_t* recv = (int32_t*)(ws + p.off_recv);
+  if (p.N > 0)
+    k_recv<<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, g->row_ptr, p.E, recv, zero_rows_of, p.C);
+  if (p.S > 1 && p.E > 0) {
+    const int64_t nb = p.n_count_blocks;
+    // block counts, then their exclusive offsets, in one region
+    int32_t* cnt = (int32_t*)(ws + p.off_blockcnt);
+    int64_t* off = (int64_t*)(ws + p.off_blockcnt + ((4 * (size_t)p.P * nb + 7) & ~size_t(7)));
+    int64_t* pair_start = (int64_t*)(ws + p.off_pair_start);
+    int32_t* perm = (int32_t*)(ws + p.off_perm);
+    k_pair_count<<<(int)nb, 256, 0, s>>>(p.E, recv, g->col, species, p.S, p.N, nb, cnt);
+    k_pair_scan<<<1, 1024, 0, s>>>(nb, p.P, cnt, off, pair_start, p.E);
+    k_pair_scatter<<<(int)nb, 256, 0, s>>>(p.E, recv, g->col, species, p.S, p.N, nb, off, perm);
+  }
+}
+
+void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
+                    const eec_model* m, int64_t e0, int64_t e1, const float* R_chunk,
+                    const float* Y_chunk, float* A, const char* ws) {
+  if (e1 <= e0) return;
+  const int32_t* recv = (const int32_t*)(ws + p.off_recv);
+  const int grid = (int)std::min<int64_t>(p.N, 2048);
+  if (p.C == 64)
+    k_message<64><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, g->col, species, m->emb, p.S, p.N,
+                                        R_chunk, Y_chunk, A);
+  else
+    k_message<128><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, g->col, species, m->emb, p.S, p.N,
+                                         R_chunk, Y_chunk, A);
+}
+
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, float* ei,
+                    double*, float* energy) {
+  if (p.N > 0) {
+    if (p.C == 64)
+      k_readout<64><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, m->w_read, A, ei);
+    else
+      k_readout<128><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, m->w_read, A, ei);
+  }
+  k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
+}
+
+void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                    const float* gin, float* forces, double* vpart, float* virial) {
+  if (p.N == 0) {
+    if (virial) k_virial_total<<<1, 1024, 0, s>>>(0, vpart, virial);
+    return;
+  }
+  if (virial) {
+    k_scatter<true><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev,
+                                                        pos, box.L[0], box.L[1], box.L[2], gin,
+                                                        forces, vpart);
+    k_virial_total<<<1, 1024, 0, s>>>(p.N, vpart, virial);
+  } else {
+    k_scatter<false><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift,
+                                                         g->rev, pos, box.L[0], box.L[1], box.L[2],
+                                                         gin, forces, nullptr);
+  }
+}
+
+void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box, double cutoff,
+                  float* r, float* basis, float* Y) {
+  if (g->n_edges == 0 || g->n_atoms == 0) return;
+  k_basis<<<blocks_for(2 * g->n_edges, 256), 256, 0, s>>>(g->n_edges, g->n_atoms, g->row_ptr, g->col,
+                                                          g->shift, pos, box.L[0], box.L[1],
+                                                          box.L[2], cutoff, r, basis, Y);
+}
+
+}  // namespace eec

@@ -1,0 +1,193 @@
+// Device building blocks shared by the gfx950 kernels of the edge convolution.
+//
+// Lane conventions (wave64, FP32 matrix cores, v_mfma_f32_32x32x2_f32):
+//   A operand lane l holds A[l % 32][l / 32], B operand lane l holds
+//   B[l / 32][l % 32], and accumulator register r of lane l holds
+//   D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// An edge tile is 32 edges; edge slot s = l % 32 and the lane half h = l / 32.
+// With edges on the N (column) side, the accumulator registers of one layer are
+// directly the B operand of the next layer (the K index is permuted the same
+// way on the weight side), so the three-layer radial chain runs without any
+// cross-lane data movement.  In that layout, register r of 32-row tile t of a
+// lane in half h holds feature 32 t + fperm(r) + 4 h of edge s.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eec {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int NB = 32;   // radial basis functions
+constexpr int HID = 64;  // hidden width of the radial network
+constexpr int NLM = 16;  // (lmax + 1)^2 harmonics, lmax = 3
+constexpr double PI = 3.14159265358979323846;
+
+// Row (within a 32-row accumulator tile, lane half 0) held by accumulator register r.
+__device__ __forceinline__ constexpr int fperm(int r) { return ((r >> 2) << 3) | (r & 3); }
+
+// Basis row index carried by row rho of the transposed-W1 tile, chosen so that a
+// lane in half h holds basis functions 16 h .. 16 h + 15 in registers 0..15.
+__device__ __forceinline__ int basis_of_row(int rho) {
+  int h = (rho >> 2) & 1;
+  int r = ((rho >> 3) << 2) | (rho & 3);
+  return 16 * h + r;
+}
+
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// XOR-swizzled row-major weight tile in LDS: element (row, col) of a matrix
+// with `ncols` columns (a multiple of 32).  Reads along a row (lanes over
+// columns) and down a column (lanes over rows) are both bank-conflict free.
+__device__ __forceinline__ int swz(int row, int col, int ncols) {
+  return row * ncols + (col ^ (row & 31));
+}
+
+// ---------------------------------------------------------------- geometry
+// d = (x_j - x_i) + n * L component-wise in binary64, r2 = (dx*dx + dy*dy) + dz*dz,
+// with no contraction into fused multiply-adds, so that the cutoff decision
+// and the edge vector are the same bits the neighbour list used.
+__device__ __forceinline__ void edge_vector(const double* __restrict__ pos, int i, int j,
+                                            const int8_t* __restrict__ sh, double Lx, double Ly,
+                                            double Lz, double d[3]) {
+#pragma clang fp contract(off)
+  d[0] = (pos[3 * j + 0] - pos[3 * i + 0]) + (double)sh[0] * Lx;
+  d[1] = (pos[3 * j + 1] - pos[3 * i + 1]) + (double)sh[1] * Ly;
+  d[2] = (pos[3 * j + 2] - pos[3 * i + 2]) + (double)sh[2] * Lz;
+}
+
+__device__ __forceinline__ double norm2_nofma(const double d[3]) {
+#pragma clang fp contract(off)
+  double r2 = (d[0] * d[0] + d[1] * d[1]) + d[2] * d[2];
+  return r2;
+}
+
+// ---------------------------------------------------------------- basis
+// Polynomial cutoff envelope of exponent 6 and its derivative (binary64).
+__device__ __forceinline__ double envelope(double x) {
+  if (x >= 1.0) return 0.0;
+  double x2 = x * x, x3 = x2 * x, x6 = x3 * x3;
+  return 1.0 + x6 * (-28.0 + x * (48.0 - 21.0 * x));
+}
+__device__ __forceinline__ double envelope_d(double x) {
+  if (x >= 1.0) return 0.0;
+  double x2 = x * x, x5 = x2 * x2 * x, om = 1.0 - x;
+  return -168.0 * x5 * om * om;
+}
+
+// Basis functions n = n0 .. n0 + 15 (1-based n0) of b_n = sin(n pi r / rc) / r * env(r / rc)
+// for one lane half, by the angle-addition recurrence in binary64 from one sincos
+// pair at n0 and one at the step angle; optionally db_n / dr.
+template <bool DERIV>
+__device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16], float db[16]) {
+  const double theta = PI / rc * r;
+  double s1, c1, s, c;
+  sincos(theta, &s1, &c1);
+  sincos((double)n0 * theta, &s, &c);
+  const double x = r / rc;
+  const double env = envelope(x);
+  const double inv_r = 1.0 / r;
+  const double envd = DERIV ? envelope_d(x) / rc : 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const double sr = s * inv_r;
+    b[k] = (float)(sr * env);
+    if (DERIV) {
+      const double kn = (double)(n0 + k) * (PI / rc);
+      db[k] = (float)((kn * c * inv_r - sr * inv_r) * env + sr * envd);
+    }
+    const double sn = s * c1 + c * s1;
+    const double cn = c * c1 - s * s1;
+    s = sn;
+    c = cn;
+  }
+}
+
+// ---------------------------------------------------------------- harmonics
+// Real component-normalised harmonics l <= 3 of a unit vector (x, y, z),
+// flat index l*l + l + m, m = -l..l, z polar, no Condon-Shortley phase.
+struct SphC {
+  static constexpr float s3 = 1.7320508075688772f;     // sqrt 3
+  static constexpr float s15 = 3.8729833462074170f;    // sqrt 15
+  static constexpr float s5h = 1.1180339887498949f;    // sqrt 5 / 2
+  static constexpr float s15h = 1.9364916731037085f;   // sqrt 15 / 2
+  static constexpr float s70q = 2.0916500663351889f;   // sqrt 70 / 4
+  static constexpr float s105 = 10.246950765959598f;   // sqrt 105
+  static constexpr float s42q = 1.6201851746019651f;   // sqrt 42 / 4
+  static constexpr float s7h = 1.3228756555322954f;    // sqrt 7 / 2
+  static constexpr float s105h = 5.1234753829797990f;  // sqrt 105 / 2
+};
+
+__device__ __forceinline__ void sph16(float x, float y, float z, float Y[16]) {
+  const float x2 = x * x, y2 = y * y, z2 = z * z;
+  Y[0] = 1.f;
+  Y[1] = SphC::s3 * y;
+  Y[2] = SphC::s3 * z;
+  Y[3] = SphC::s3 * x;
+  Y[4] = SphC::s15 * x * y;
+  Y[5] = SphC::s15 * y * z;
+  Y[6] = SphC::s5h * (3.f * z2 - 1.f);
+  Y[7] = SphC::s15 * x * z;
+  Y[8] = SphC::s15h * (x2 - y2);
+  Y[9] = SphC::s70q * y * (3.f * x2 - y2);
+  Y[10] = SphC::s105 * x * y * z;
+  Y[11] = SphC::s42q * y * (5.f * z2 - 1.f);
+  Y[12] = SphC::s7h * z * (5.f * z2 - 3.f);
+  Y[13] = SphC::s42q * x * (5.f * z2 - 1.f);
+  Y[14] = SphC::s105h * z * (x2 - y2);
+  Y[15] = SphC::s70q * x * (x2 - 3.f * y2);
+}
+
+// G = sum_k w_k grad P_k(x, y, z) of the polynomials above (before projection
+// onto the tangent plane of the unit sphere).
+__device__ __forceinline__ void sph16_grad_dot(float x, float y, float z, const float w[16],
+                                               float G[3]) {
+  const float x2 = x * x, y2 = y * y, z2 = z * z;
+  float gx = 0.f, gy = 0.f, gz = 0.f;
+  gy += w[1] * SphC::s3;
+  gz += w[2] * SphC::s3;
+  gx += w[3] * SphC::s3;
+  gx += w[4] * SphC::s15 * y;          gy += w[4] * SphC::s15 * x;
+  gy += w[5] * SphC::s15 * z;          gz += w[5] * SphC::s15 * y;
+  gz += w[6] * SphC::s5h * 6.f * z;
+  gx += w[7] * SphC::s15 * z;          gz += w[7] * SphC::s15 * x;
+  gx += w[8] * SphC::s15h * 2.f * x;   gy -= w[8] * SphC::s15h * 2.f * y;
+  gx += w[9] * SphC::s70q * 6.f * x * y;
+  gy += w[9] * SphC::s70q * 3.f * (x2 - y2);
+  gx += w[10] * SphC::s105 * y * z;    gy += w[10] * SphC::s105 * x * z;
+  gz += w[10] * SphC::s105 * x * y;
+  gy += w[11] * SphC::s42q * (5.f * z2 - 1.f);
+  gz += w[11] * SphC::s42q * 10.f * y * z;
+  gz += w[12] * SphC::s7h * (15.f * z2 - 3.f);
+  gx += w[13] * SphC::s42q * (5.f * z2 - 1.f);
+  gz += w[13] * SphC::s42q * 10.f * x * z;
+  gx += w[14] * SphC::s105h * 2.f * x * z;
+  gy -= w[14] * SphC::s105h * 2.f * y * z;
+  gz += w[14] * SphC::s105h * (x2 - y2);
+  gx += w[15] * SphC::s70q * 3.f * (x2 - y2);
+  gy -= w[15] * SphC::s70q * 6.f * x * y;
+  G[0] = gx;
+  G[1] = gy;
+  G[2] = gz;
+}
+
+// ---------------------------------------------------------------- activations
+__device__ __forceinline__ float sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+__device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
+__device__ __forceinline__ float silu_d(float z) {
+  const float s = sigmoid(z);
+  return s * (1.f + z * (1.f - s));
+}
+
+}  // namespace eec

@@ -1,0 +1,88 @@
+// Internal host-side interfaces between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/eec.h"
+
+namespace eec {
+
+// Error bits raised on the device by the neighbour builder.
+enum : uint32_t {
+  FLAG_OUT_OF_BOX = 1u,
+  FLAG_SPECIES = 2u,
+  FLAG_GEOMETRY = 4u,
+};
+
+struct Box {
+  double L[3];
+};
+
+// ---- neighbour list
+struct NbPlan {
+  int32_t nc[3];
+  int64_t n_cells;
+  size_t bytes;
+  // byte offsets into the workspace
+  size_t off_cell_count, off_cell_fill, off_cell_start, off_cell_atoms, off_cell_of, off_deg,
+      off_scratch;
+};
+NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff);
+
+// Runs the whole builder; returns EEC_OK / error.  Writes *n_edges.
+eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n_atoms, const double* pos,
+                    const double* box, double cutoff, const int32_t* species, int32_t n_species,
+                    int64_t cap, int32_t* row_ptr, int32_t* col, int8_t* shift, int32_t* rev,
+                    int64_t* n_edges, char* ws, const char** why);
+
+// ---- edge-convolution workspace plan
+struct ConvPlan {
+  int C, NC, S, P;
+  int64_t E;
+  int32_t N;
+  int64_t chunk;  // edges per streamed chunk
+  size_t bytes;
+  size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_A, off_R, off_Y, off_g, off_epart,
+      off_vpart, off_ei;
+  int64_t n_count_blocks;
+};
+ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
+
+// Graph preparation: receiver of each edge; pair-grouped edge order when S > 1.
+void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
+                    char* ws, float* zero_rows_of /* [N][16][C] or NULL */);
+
+// Radial network over a range of edges.  When `basis_in` is given the basis is
+// read from it (materialising entry point); otherwise it is computed from the
+// geometry.  Writes R rows (relative to e_begin) and, if Y_out, harmonics rows.
+void launch_radial(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                   Box box, double cutoff, const int32_t* species, const eec_model* m,
+                   const float* basis_in, int64_t e_begin, int64_t e_end, float* R_out,
+                   float* Y_out, const char* ws);
+
+// Streaming message of one chunk [e_begin, e_end) into A (assign or accumulate per row).
+void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
+                    const eec_model* m, int64_t e_begin, int64_t e_end, const float* R_chunk,
+                    const float* Y_chunk, float* A, const char* ws);
+
+// Readout: E_i (into ei), per-block energy partials, Abar = 2 w A in place.
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, float* ei,
+                    double* epart, float* energy);
+
+// Backward over all edges: g = dE/dd.
+void launch_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                     Box box, double cutoff, const int32_t* species, const eec_model* m,
+                     const float* Abar, float* gout, const char* ws);
+
+// Force scatter (and optional virial).
+void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                    Box box, const float* gin, float* forces, double* vpart, float* virial);
+
+// Materialised basis / harmonics.
+void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box, double cutoff,
+                  float* r, float* basis, float* Y);
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace eec

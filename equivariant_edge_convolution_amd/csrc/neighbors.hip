@@ -1,0 +1,342 @@
+// Cell-list neighbour builder emitting receiver-sorted CSR with reverse edges.
+//
+// Edge set: every (i, j, n), n in {-1,0,1}^3, with d = (x_j - x_i) + n L in
+// binary64 and (dx*dx + dy*dy) + dz*dz < rc*rc, excluding (i, i, 0).  The list
+// is rebuilt beside the force call in an MD loop ("FastMACE rewrite screens",
+// OPT2-T04 overlap_rebuild); the pages do not fix an order, so rows are sorted
+// by (j, nx, ny, nz), which makes the output independent of thread timing.
+//
+// Pipeline (one host synchronisation, after the row counts):
+//   bin atoms into cells of side >= rc  ->  exclusive scan of cell counts  ->
+//   place atoms  ->  count edges per row (one wave per receiver, lanes over the
+//   27 neighbouring (cell, image) candidates)  ->  scan  ->  [sync: E, flags]
+//   ->  fill each row with (j, n) keys  ->  rank-sort each row  ->  reverse index.
+#include <math.h>
+
+#include <algorithm>
+
+#include "eec_device.hpp"
+#include "eec_internal.hpp"
+
+namespace eec {
+
+namespace {
+
+constexpr int SORT_LDS = 2048;  // keys a row-sort wave stages in LDS
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+       k += (int64_t)gridDim.x * blockDim.x)
+    p[k] = v;
+}
+
+__global__ void k_nb_bin(int32_t n, const double* __restrict__ pos, double Lx, double Ly, double Lz,
+                         int nc0, int nc1, int nc2, const int32_t* __restrict__ species,
+                         int32_t n_species, int32_t* __restrict__ cell_of,
+                         uint32_t* __restrict__ cell_count, uint32_t* __restrict__ flags) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double x = pos[3 * i], y = pos[3 * i + 1], z = pos[3 * i + 2];
+  const bool ok = isfinite(x) && isfinite(y) && isfinite(z) && x >= 0.0 && y >= 0.0 && z >= 0.0 &&
+                  x < Lx && y < Ly && z < Lz;
+  int c = 0;
+  if (!ok) {
+    atomicOr(flags, FLAG_OUT_OF_BOX);
+  } else {
+    const int cx = min((int)(x * ((double)nc0 / Lx)), nc0 - 1);
+    const int cy = min((int)(y * ((double)nc1 / Ly)), nc1 - 1);
+    const int cz = min((int)(z * ((double)nc2 / Lz)), nc2 - 1);
+    c = (cx * nc1 + cy) * nc2 + cz;
+  }
+  if (species != nullptr) {
+    const int32_t zs = species[i];
+    if (zs < 0 || zs >= n_species) atomicOr(flags, FLAG_SPECIES);
+  }
+  cell_of[i] = c;
+  atomicAdd(&cell_count[c], 1u);
+}
+
+// Exclusive scan of n unsigned counts into out[0..n] (out[n] = total) with one
+// workgroup of 1024 threads; also stores the total as int64 when asked.
+__global__ void __launch_bounds__(1024) k_scan_excl(const uint32_t* __restrict__ in, int64_t n,
+                                                    int32_t* __restrict__ out,
+                                                    int64_t* __restrict__ total) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = std::min<int64_t>(n, t * per), b = std::min<int64_t>(n, a + per);
+  int64_t s = 0;
+  for (int64_t k = a; k < b; ++k) s += in[k];
+  part[t] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 thread sums (fixed order).
+  for (int off = 1; off < 1024; off <<= 1) {
+    int64_t v = (t >= off) ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = part[t] - s;
+  for (int64_t k = a; k < b; ++k) {
+    out[k] = (int32_t)run;
+    run += in[k];
+  }
+  if (t == 1023) {
+    out[n] = (int32_t)part[1023];
+    if (total) *total = part[1023];
+  }
+}
+
+__global__ void k_cell_place(int32_t n, const int32_t* __restrict__ cell_of,
+                             const int32_t* __restrict__ cell_start,
+                             uint32_t* __restrict__ cell_fill, int32_t* __restrict__ cell_atoms) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int c = cell_of[i];
+  const uint32_t slot = atomicAdd(&cell_fill[c], 1u);
+  cell_atoms[cell_start[c] + slot] = i;
+}
+
+struct Grid {
+  int nc0, nc1, nc2;
+  double Lx, Ly, Lz, rc2;
+};
+
+// Visit every candidate (j, image) of receiver i; lanes stride over the
+// members of each of the 27 neighbouring cells.  f(keep, j, s, r2).
+template <class F>
+__device__ __forceinline__ void for_candidates(int i, const Grid& gr, const double* __restrict__ pos,
+                                               const int32_t* __restrict__ cell_of,
+                                               const int32_t* __restrict__ cell_start,
+                                               const int32_t* __restrict__ cell_atoms, int lane,
+                                               F&& f) {
+  const int ci = cell_of[i];
+  const int cz = ci % gr.nc2, cy = (ci / gr.nc2) % gr.nc1, cx = ci / (gr.nc2 * gr.nc1);
+  for (int o = 0; o < 27; ++o) {
+    const int vx = cx + o / 9 - 1, vy = cy + (o / 3) % 3 - 1, vz = cz + o % 3 - 1;
+    const int ix = vx < 0 ? -1 : (vx >= gr.nc0 ? 1 : 0);
+    const int iy = vy < 0 ? -1 : (vy >= gr.nc1 ? 1 : 0);
+    const int iz = vz < 0 ? -1 : (vz >= gr.nc2 ? 1 : 0);
+    const int wx = vx - ix * gr.nc0, wy = vy - iy * gr.nc1, wz = vz - iz * gr.nc2;
+    const int c2 = (wx * gr.nc1 + wy) * gr.nc2 + wz;
+    const int s = (ix + 1) * 9 + (iy + 1) * 3 + (iz + 1);
+    const int a = cell_start[c2], b = cell_start[c2 + 1];
+    for (int base = a; base < b; base += 64) {
+      const int k = base + lane;
+      bool keep = false;
+      int j = 0;
+      double r2 = 1.0;
+      if (k < b) {
+        j = cell_atoms[k];
+        int8_t sh[3] = {(int8_t)ix, (int8_t)iy, (int8_t)iz};
+        double d[3];
+        edge_vector(pos, i, j, sh, gr.Lx, gr.Ly, gr.Lz, d);
+        r2 = norm2_nofma(d);
+        keep = (r2 < gr.rc2) && !(j == i && s == 13);
+      }
+      f(keep, j, s, r2);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_nb_count(int32_t n, Grid gr, const double* __restrict__ pos,
+                                                  const int32_t* __restrict__ cell_of,
+                                                  const int32_t* __restrict__ cell_start,
+                                                  const int32_t* __restrict__ cell_atoms,
+                                                  uint32_t* __restrict__ deg,
+                                                  uint32_t* __restrict__ flags) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  uint32_t cnt = 0;
+  bool coincident = false;
+  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, lane,
+                 [&](bool keep, int, int, double r2) {
+                   cnt += keep ? 1u : 0u;
+                   coincident |= keep && (r2 == 0.0);
+                 });
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if (coincident) atomicOr(flags, FLAG_GEOMETRY);
+  if (lane == 0) deg[i] = cnt;
+}
+
+// Writes the unsorted (j * 27 + s) keys of each row into `keys` at its CSR slots.
+__global__ void __launch_bounds__(256) k_nb_fill(int32_t n, Grid gr, const double* __restrict__ pos,
+                                                 const int32_t* __restrict__ cell_of,
+                                                 const int32_t* __restrict__ cell_start,
+                                                 const int32_t* __restrict__ cell_atoms,
+                                                 const int32_t* __restrict__ rp,
+                                                 int32_t* __restrict__ keys) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  int base = rp[i];
+  const int end = rp[i + 1];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, lane,
+                 [&](bool keep, int j, int s, double) {
+                   const uint64_t mask = __ballot(keep);
+                   const int at = base + __popcll(mask & below);
+                   if (keep && at < end) keys[at] = j * 27 + s;
+                   base += __popcll(mask);
+                 });
+}
+
+// One 64-thread workgroup per row: rank-sort the row's distinct keys and
+// write the sorted senders and image shifts.
+__global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __restrict__ rp,
+                                                const int32_t* __restrict__ keys,
+                                                int32_t* __restrict__ col, int8_t* __restrict__ shift) {
+  __shared__ int32_t sk[SORT_LDS];
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (i >= n) return;
+  const int a = rp[i], deg = rp[i + 1] - a;
+  const bool in_lds = deg <= SORT_LDS;
+  if (in_lds)
+    for (int k = lane; k < deg; k += 64) sk[k] = keys[a + k];
+  __syncthreads();
+  const int32_t* src = in_lds ? sk : keys + a;
+  for (int k = lane; k < deg; k += 64) {
+    const int32_t key = src[k];
+    int rank = 0;
+    for (int q = 0; q < deg; ++q) rank += (src[q] < key) ? 1 : 0;
+    const int s = key % 27;
+    col[a + rank] = key / 27;
+    shift[3 * (a + rank) + 0] = (int8_t)(s / 9 - 1);
+    shift[3 * (a + rank) + 1] = (int8_t)((s / 3) % 3 - 1);
+    shift[3 * (a + rank) + 2] = (int8_t)(s % 3 - 1);
+  }
+}
+
+__device__ __forceinline__ int32_t key_at(const int32_t* __restrict__ col,
+                                          const int8_t* __restrict__ shift, int e) {
+  return col[e] * 27 + (shift[3 * e] + 1) * 9 + (shift[3 * e + 1] + 1) * 3 + (shift[3 * e + 2] + 1);
+}
+
+// One wave per row: rev(e) = index of (j, i, -n) found by binary search in row j.
+__global__ void __launch_bounds__(256) k_nb_rev(int32_t n, const int32_t* __restrict__ rp,
+                                                const int32_t* __restrict__ col,
+                                                const int8_t* __restrict__ shift,
+                                                int32_t* __restrict__ rev,
+                                                uint32_t* __restrict__ flags) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  for (int e = rp[i] + lane; e < rp[i + 1]; e += 64) {
+    const int j = col[e];
+    const int s = (shift[3 * e] + 1) * 9 + (shift[3 * e + 1] + 1) * 3 + (shift[3 * e + 2] + 1);
+    const int32_t target = i * 27 + (26 - s);
+    int lo = rp[j], hi = rp[j + 1];
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_at(col, shift, mid) < target) lo = mid + 1; else hi = mid;
+    }
+    if (lo < rp[j + 1] && key_at(col, shift, lo) == target) {
+      rev[e] = lo;
+    } else {
+      rev[e] = e;
+      atomicOr(flags, FLAG_GEOMETRY);
+    }
+  }
+}
+
+__global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int64_t n) {
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+       k += (int64_t)gridDim.x * blockDim.x)
+    dst[k] = src[k];
+}
+
+inline int blocks_for(int64_t n, int per) { return (int)std::max<int64_t>(1, (n + per - 1) / per); }
+
+}  // namespace
+
+NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff) {
+  NbPlan p{};
+  int64_t nc[3];
+  for (int k = 0; k < 3; ++k) {
+    double q = floor(box[k] / (cutoff * (1.0 + 1e-9)));
+    nc[k] = (q >= 1.0 && q < 1e6) ? (int64_t)q : 1;
+  }
+  // Keep the grid proportional to the atom count; a coarser grid stays exact.
+  const int64_t cap = 2 * (int64_t)std::max(n_atoms, 1) + 64;
+  while (nc[0] * nc[1] * nc[2] > cap) {
+    int k = (nc[0] >= nc[1] && nc[0] >= nc[2]) ? 0 : (nc[1] >= nc[2] ? 1 : 2);
+    nc[k] = std::max<int64_t>(1, nc[k] - 1);
+  }
+  for (int k = 0; k < 3; ++k) p.nc[k] = (int32_t)nc[k];
+  p.n_cells = nc[0] * nc[1] * nc[2];
+  const int64_t N = std::max(n_atoms, 0);
+  size_t o = 0;
+  p.off_cell_count = o; o += align256(sizeof(uint32_t) * p.n_cells);
+  p.off_cell_fill = o;  o += align256(sizeof(uint32_t) * p.n_cells);
+  p.off_cell_start = o; o += align256(sizeof(int32_t) * (p.n_cells + 1));
+  p.off_cell_atoms = o; o += align256(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  p.off_cell_of = o;    o += align256(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  p.off_deg = o;        o += align256(sizeof(uint32_t) * (N + 1) + sizeof(int32_t) * (N + 1));
+  p.off_scratch = o;    o += 256;
+  p.bytes = o;
+  return p;
+}
+
+eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos, const double* box,
+                    double cutoff, const int32_t* species, int32_t n_species, int64_t cap,
+                    int32_t* row_ptr, int32_t* col, int8_t* shift, int32_t* rev, int64_t* n_edges,
+                    char* ws, const char** why) {
+  uint32_t* cell_count = (uint32_t*)(ws + p.off_cell_count);
+  uint32_t* cell_fill = (uint32_t*)(ws + p.off_cell_fill);
+  int32_t* cell_start = (int32_t*)(ws + p.off_cell_start);
+  int32_t* cell_atoms = (int32_t*)(ws + p.off_cell_atoms);
+  int32_t* cell_of = (int32_t*)(ws + p.off_cell_of);
+  uint32_t* deg = (uint32_t*)(ws + p.off_deg);
+  int32_t* rp_tmp = (int32_t*)(ws + p.off_deg + sizeof(uint32_t) * (n + 1));
+  uint32_t* flags = (uint32_t*)(ws + p.off_scratch);
+  int64_t* total = (int64_t*)(ws + p.off_scratch + 8);
+
+  const int64_t nc = p.n_cells;
+  k_fill_u32<<<blocks_for(2 * nc, 256), 256, 0, s>>>(cell_count, nc, 0u);
+  k_fill_u32<<<blocks_for(nc, 256), 256, 0, s>>>(cell_fill, nc, 0u);
+  k_fill_u32<<<1, 64, 0, s>>>(flags, 4, 0u);
+  if (n > 0) {
+    k_nb_bin<<<blocks_for(n, 256), 256, 0, s>>>(n, pos, box[0], box[1], box[2], p.nc[0], p.nc[1],
+                                                 p.nc[2], species, n_species, cell_of, cell_count,
+                                                 flags);
+  }
+  k_scan_excl<<<1, 1024, 0, s>>>(cell_count, nc, cell_start, nullptr);
+  Grid gr{p.nc[0], p.nc[1], p.nc[2], box[0], box[1], box[2], cutoff * cutoff};
+  if (n > 0) {
+    k_cell_place<<<blocks_for(n, 256), 256, 0, s>>>(n, cell_of, cell_start, cell_fill, cell_atoms);
+    k_nb_count<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, deg,
+                                                 flags);
+  }
+  k_scan_excl<<<1, 1024, 0, s>>>(deg, n, rp_tmp, total);
+  struct {
+    uint32_t flags;
+    uint32_t pad;
+    int64_t total;
+  } host{};
+  if (hipMemcpyAsync(&host.flags, flags, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(&host.total, total, 8, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    *why = "HIP error while reading the edge count";
+    return EEC_ERR_HIP;
+  }
+  if (host.flags & FLAG_OUT_OF_BOX) { *why = "a position is non-finite or outside [0, L)"; return EEC_ERR_OUT_OF_BOX; }
+  if (host.flags & FLAG_SPECIES) { *why = "a species index is outside [0, n_species)"; return EEC_ERR_SPECIES; }
+  if (host.flags & FLAG_GEOMETRY) { *why = "two atoms (or periodic images) coincide"; return EEC_ERR_GEOMETRY; }
+  *n_edges = host.total;
+  if (host.total > cap) { *why = "edge_capacity is smaller than the edge count"; return EEC_ERR_CAPACITY; }
+  if (host.total > INT32_MAX) { *why = "edge count exceeds int32 indexing"; return EEC_ERR_SHAPE; }
+
+  k_copy_i32<<<blocks_for(n + 1, 256), 256, 0, s>>>(rp_tmp, row_ptr, n + 1);
+  if (n > 0 && host.total > 0) {
+    k_nb_fill<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, row_ptr,
+                                                rev /* keys staged here */);
+    k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, rev, col, shift);
+    k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev, flags);
+  }
+  if (hipGetLastError() != hipSuccess) { *why = "kernel launch failed"; return EEC_ERR_HIP; }
+  return EEC_OK;
+}
+
+}  // namespace eec

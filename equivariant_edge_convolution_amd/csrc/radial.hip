@@ -1,0 +1,492 @@
+// FP32 matrix-core kernels of the radial network.
+//
+//  k_radial   : geometry -> basis (or a given basis) -> z1 = b W1 -> silu ->
+//               z2 = s1 W2 -> silu -> R = s2 W3, per 32-edge tile, writing R
+//               rows (and harmonics rows) of a chunk of edges.  The chain
+//               (E,4,32) -> (E,4,64) -> (E,256) is the radial projection of
+//               "deepmd-kit PR #6108", What; it is compute-bound there
+//               ("deepmd-kit PR #6108", Why not a fused Triton kernel) and runs
+//               here on v_mfma_f32_32x32x2_f32 with weights staged in LDS.
+//  k_backward : the matching input-gradient backward per edge tile
+//               ("deepmd-kit PR #2", Implementation and scope: finish the
+//               reverse chain of one edge cohort before the next), recomputing
+//               the forward activations instead of storing them:
+//                 Rbar_{l,c} = h_c sum_m Abar_{i,lm,c} Y_lm,
+//                 Ybar_lm    = sum_c Abar_{i,lm,c} h_c R_{l,c},
+//                 s2bar = Rbar W3^T, z2bar = s2bar silu'(z2), s1bar = z2bar W2^T,
+//                 z1bar = s1bar silu'(z1), bbar = z1bar W1^T,
+//                 rbar = sum_n bbar_n db_n/dr,
+//                 g = rbar u + (I - u u^T) (sum_lm Ybar_lm grad Y_lm) / r.
+//
+// Work decomposition: edges are taken in pair-grouped order (one weight set per
+// tile), in 32-edge tiles, one tile per wave; a workgroup of W waves holds one
+// pair's weights in LDS and walks "batches" of W tiles of that pair, grid-stride.
+#include <algorithm>
+
+#include "eec_device.hpp"
+#include "eec_internal.hpp"
+
+namespace eec {
+namespace {
+
+constexpr int MAXP = 16;
+
+// Weights in LDS, row-major with one padding column: a wave reading along a row
+// (lanes over columns) or down a column (lanes over rows) touches 32 distinct
+// banks either way, and every address is a per-lane base plus an immediate.
+constexpr int LDH = HID + 1;  // row stride of W1 [32][64] and W2 [64][64]
+template <int C>
+struct Lds {
+  static constexpr int NC = 4 * C;
+  static constexpr int LD3 = NC + 1;            // row stride of W3 [64][NC]
+  static constexpr int W1 = 0;
+  static constexpr int W2 = W1 + NB * LDH;
+  static constexpr int W3 = W2 + HID * LDH;
+  static constexpr int FLOATS = W3 + HID * LD3;  // 90752 B (C=64), 156288 B (C=128)
+};
+
+struct EdgeIn {
+  const double* pos;
+  double Lx, Ly, Lz, rc;
+  const int32_t* recv;
+  const int32_t* col;
+  const int8_t* shift;
+  const int32_t* species;
+  int32_t n_atoms;
+  int64_t n_edges;
+};
+
+struct Sched {
+  const int32_t* perm;        // pair-grouped order -> CSR edge; NULL = identity
+  const int64_t* pair_start;  // [P+1] group offsets in that order; NULL = one group [0, E)
+  int P;
+  int64_t e0, e1;             // CSR edge range to process
+};
+
+struct SchedState {
+  int64_t q0[MAXP], q1[MAXP];
+  int bstart[MAXP + 1];
+  int ntile[MAXP];
+};
+
+// Lower bound of CSR index `e` among positions [lo, hi) of a pair group.
+__device__ int64_t group_lower_bound(const int32_t* perm, int64_t lo, int64_t hi, int64_t e) {
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)perm[mid] < e) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+template <int W>
+__device__ void sched_init(const Sched& sc, SchedState& st) {
+  const int t = threadIdx.x;
+  if (t < sc.P) {
+    int64_t q0, q1;
+    if (sc.perm == nullptr) {
+      q0 = sc.e0;
+      q1 = sc.e1;
+    } else {
+      const int64_t g0 = sc.pair_start[t], g1 = sc.pair_start[t + 1];
+      q0 = group_lower_bound(sc.perm, g0, g1, sc.e0);
+      q1 = group_lower_bound(sc.perm, q0, g1, sc.e1);
+    }
+    st.q0[t] = q0;
+    st.q1[t] = q1;
+    st.ntile[t] = (int)((q1 - q0 + 31) / 32);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int p = 0; p < sc.P; ++p) {
+      st.bstart[p] = acc;
+      acc += (st.ntile[p] + W - 1) / W;
+    }
+    st.bstart[sc.P] = acc;
+  }
+  __syncthreads();
+}
+
+template <int C>
+__device__ void stage_weights(float* lds, const float* __restrict__ W1, const float* __restrict__ W2,
+                              const float* __restrict__ W3, int p) {
+  constexpr int NC = Lds<C>::NC;
+  const float* w1 = W1 + (size_t)p * NB * HID;
+  const float* w2 = W2 + (size_t)p * HID * HID;
+  const float* w3 = W3 + (size_t)p * HID * NC;
+  for (int k = threadIdx.x; k < NB * HID; k += blockDim.x)
+    lds[Lds<C>::W1 + (k / HID) * LDH + k % HID] = w1[k];
+  for (int k = threadIdx.x; k < HID * HID; k += blockDim.x)
+    lds[Lds<C>::W2 + (k / HID) * LDH + k % HID] = w2[k];
+  for (int k = threadIdx.x; k < HID * NC; k += blockDim.x)
+    lds[Lds<C>::W3 + (k / NC) * Lds<C>::LD3 + k % NC] = w3[k];
+}
+
+// Input hidden feature of K-step ks (0..31) carried by a lane of half h when the
+// 64 hidden features sit in two edges-on-N accumulator tiles: hid_k0(ks) + 4 h.
+__device__ __forceinline__ constexpr int hid_k0(int ks) { return 32 * (ks >> 4) + fperm(ks & 15); }
+
+// z1 = b W1 (edges on N): two 32-feature tiles.
+__device__ __forceinline__ void layer1(const float* __restrict__ w1s, const float b[16], int s, int h,
+                                       f32x16 z[2]) {
+  const float* w = w1s + 16 * h * LDH + s;  // W1[16 h + ks][32 m + s]
+  z[0] = zero16();
+  z[1] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) z[m] = mfma32(w[ks * LDH + 32 * m], b[ks], z[m]);
+}
+
+// z2 = s1 W2 (edges on N).
+__device__ __forceinline__ void layer2(const float* __restrict__ w2s, const f32x16 s1[2], int s, int h,
+                                       f32x16 z[2]) {
+  const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
+  z[0] = zero16();
+  z[1] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) {
+    const float bv = s1[ks >> 4][ks & 15];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) z[m] = mfma32(w[hid_k0(ks) * LDH + 32 * m], bv, z[m]);
+  }
+}
+
+__device__ __forceinline__ void silu_tiles(const f32x16 z[2], f32x16 s[2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[m][r] = silu(z[m][r]);
+}
+
+// Geometry of the edge a lane works on (binary64, as the neighbour list).
+struct Geo {
+  double r;
+  float ux, uy, uz, inv_r;
+  int i, j;
+};
+
+__device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) {
+  Geo g;
+  int i = in.recv[e], j = in.col[e];
+  i = min(max(i, 0), in.n_atoms - 1);
+  j = min(max(j, 0), in.n_atoms - 1);
+  double d[3];
+  edge_vector(in.pos, i, j, in.shift + 3 * e, in.Lx, in.Ly, in.Lz, d);
+  const double r2 = norm2_nofma(d);
+  const double r = sqrt(r2);
+  const double ir = 1.0 / r;
+  g.r = r;
+  g.inv_r = (float)ir;
+  g.ux = (float)(d[0] * ir);
+  g.uy = (float)(d[1] * ir);
+  g.uz = (float)(d[2] * ir);
+  g.i = i;
+  g.j = j;
+  return g;
+}
+
+// ------------------------------------------------------------------ forward
+template <int C, int W, bool BASIS_IN>
+__global__ void __launch_bounds__(64 * W)
+k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restrict__ W2,
+         const float* __restrict__ W3, const float* __restrict__ basis_in, int64_t row_base,
+         float* __restrict__ R_out, float* __restrict__ Y_out) {
+  constexpr int NC = Lds<C>::NC;
+  __shared__ float lds[Lds<C>::FLOATS];
+  __shared__ SchedState st;
+  sched_init<W>(sc, st);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = lane & 31, h = lane >> 5;
+  const float* w1s = lds + Lds<C>::W1;
+  const float* w2s = lds + Lds<C>::W2;
+  const float* w3s = lds + Lds<C>::W3;
+  int loaded = -1;
+  const int nb = st.bstart[sc.P];
+  for (int b = blockIdx.x; b < nb; b += gridDim.x) {
+    int p = 0;
+    while (p + 1 < sc.P && st.bstart[p + 1] <= b) ++p;
+    if (p != loaded) {
+      __syncthreads();
+      stage_weights<C>(lds, W1, W2, W3, p);
+      __syncthreads();
+      loaded = p;
+    }
+    const int tile = (b - st.bstart[p]) * W + wave;
+    if (tile >= st.ntile[p]) continue;
+    const int64_t q = st.q0[p] + (int64_t)tile * 32 + s;
+    const bool valid = q < st.q1[p];
+    const int64_t qq = valid ? q : st.q0[p];
+    const int64_t e = sc.perm ? (int64_t)sc.perm[qq] : qq;
+
+    float bas[16];
+    const Geo g = edge_geo(in, e);
+    if (BASIS_IN) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) bas[k] = basis_in[e * NB + 16 * h + k];
+    } else {
+      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+    }
+    if (Y_out != nullptr && valid) {
+      float Y[16];
+      sph16(g.ux, g.uy, g.uz, Y);
+      float* yo = Y_out + (e - row_base) * NLM + 8 * h;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) yo[k] = Y[8 * h + k];
+    }
+    f32x16 z[2], a[2];
+    layer1(w1s, bas, s, h, z);
+    silu_tiles(z, a);
+    layer2(w2s, a, s, h, z);
+    silu_tiles(z, a);  // a = s2 (edges on N; as the A operand: edge = s)
+
+    // output row of the edge held by accumulator register r (edge slot fperm(r) + 4h)
+    const int my_row = valid ? (int)(e - row_base) : -1;
+    int orow[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) orow[r] = __shfl(my_row, fperm(r) + 4 * h);
+
+    // R = s2 W3 with edges on M: D[edge][feature], lane = feature 32 t + s.
+    constexpr int LD3 = Lds<C>::LD3;
+    const float* w3 = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
+#pragma unroll 1
+    for (int t = 0; t < NC / 32; ++t, w3 += 32) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) acc = mfma32(a[ks >> 4][ks & 15], w3[hid_k0(ks) * LD3], acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (orow[r] >= 0) R_out[(size_t)orow[r] * NC + 32 * t + s] = acc[r];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ backward
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restrict__ W2,
+           const float* __restrict__ W3, const float* __restrict__ emb, int n_species,
+           const float* __restrict__ Abar, float* __restrict__ gout) {
+  constexpr int NC = Lds<C>::NC;
+  __shared__ float lds[Lds<C>::FLOATS];
+  __shared__ SchedState st;
+  sched_init<W>(sc, st);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = lane & 31, h = lane >> 5;
+  const float* w1s = lds + Lds<C>::W1;
+  const float* w2s = lds + Lds<C>::W2;
+  const float* w3s = lds + Lds<C>::W3;
+  int loaded = -1;
+  const int nb = st.bstart[sc.P];
+  for (int b = blockIdx.x; b < nb; b += gridDim.x) {
+    int p = 0;
+    while (p + 1 < sc.P && st.bstart[p + 1] <= b) ++p;
+    if (p != loaded) {
+      __syncthreads();
+      stage_weights<C>(lds, W1, W2, W3, p);
+      __syncthreads();
+      loaded = p;
+    }
+    const int tile = (b - st.bstart[p]) * W + wave;
+    if (tile >= st.ntile[p]) continue;
+    const int64_t q = st.q0[p] + (int64_t)tile * 32 + s;
+    const bool valid = q < st.q1[p];
+    const int64_t qq = valid ? q : st.q0[p];
+    const int64_t e = sc.perm ? (int64_t)sc.perm[qq] : qq;
+    const int zj = p % n_species;
+
+    const Geo g = edge_geo(in, e);
+    float bas[16], dbas[16], Y[16];
+    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
+    sph16(g.ux, g.uy, g.uz, Y);
+
+    f32x16 z[2], a[2];
+    layer1(w1s, bas, s, h, z);
+    silu_tiles(z, a);
+    layer2(w2s, a, s, h, z);
+    silu_tiles(z, a);  // a = s2
+
+    const float* abar = Abar + (size_t)g.i * NLM * C;
+    const float* hrow = emb + (size_t)zj * C;
+    f32x16 sb[2];
+    sb[0] = zero16();
+    sb[1] = zero16();
+    float ybp[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ybp[k] = 0.f;
+
+    constexpr int LD3 = Lds<C>::LD3;
+    const float* w3r = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
+    const float* w3c = w3s + s * LD3 + 4 * h;  // W3[32 m + s][32 t + fperm(ks) + 4 h]
+#pragma unroll 1
+    for (int t = 0; t < NC / 32; ++t, w3r += 32, w3c += 32) {
+      // R tile (edges on N): register r = feature 32 t + fperm(r) + 4h of edge s
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) acc = mfma32(w3r[hid_k0(ks) * LD3], a[ks >> 4][ks & 15], acc);
+      const int ldeg = (32 * t) / C;
+      const int cb = (32 * t) % C + 4 * h;
+      float hv[16], rb[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *reinterpret_cast<const float4*>(hrow + cb + 8 * q4);
+        hv[4 * q4 + 0] = v.x; hv[4 * q4 + 1] = v.y; hv[4 * q4 + 2] = v.z; hv[4 * q4 + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[r] *= hv[r];  // rho = R h
+        rb[r] = 0.f;
+      }
+      const int lm0 = ldeg * ldeg;
+      for (int mm = 0; mm < 2 * ldeg + 1; ++mm) {
+        const int lm = lm0 + mm;
+        const float* ar = abar + lm * C + cb;
+        float av[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v = *reinterpret_cast<const float4*>(ar + 8 * q4);
+          av[4 * q4 + 0] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
+        }
+        float yb = 0.f;
+        const float ylm = Y[lm];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          yb += av[r] * acc[r];
+          rb[r] += av[r] * ylm;
+        }
+        ybp[lm] += yb;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rb[r] *= hv[r];
+      // s2bar += W3[:, tile t] Rbar_t (edges on N)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) sb[m] = mfma32(w3c[32 * m * LD3 + fperm(ks)], rb[ks], sb[m]);
+    }
+    float yb[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) yb[k] = ybp[k] + __shfl_xor(ybp[k], 32);
+
+    // recompute z1, z2 (fewer live registers through the loop above)
+    f32x16 z1[2], s1[2];
+    layer1(w1s, bas, s, h, z1);
+    silu_tiles(z1, s1);
+    layer2(w2s, s1, s, h, z);  // z = z2
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[m][r] *= silu_d(z[m][r]);  // z2bar
+    // s1bar = z2bar W2^T
+    f32x16 s1b[2];
+    s1b[0] = zero16();
+    s1b[1] = zero16();
+    const float* w2c = w2s + s * LDH + 4 * h;  // W2[32 m + s][hid_k0(ks) + 4 h]
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      const float bv = sb[ks >> 4][ks & 15];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) s1b[m] = mfma32(w2c[32 * m * LDH + hid_k0(ks)], bv, s1b[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s1b[m][r] *= silu_d(z1[m][r]);  // z1bar
+    // bbar = z1bar W1^T; row rho carries basis basis_of_row(rho)
+    f32x16 bb = zero16();
+    const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;  // W1[basis_of_row(s)][hid_k0(ks) + 4 h]
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) bb = mfma32(w1c[hid_k0(ks)], s1b[ks >> 4][ks & 15], bb);
+    float rbar = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
+    rbar += __shfl_xor(rbar, 32);
+
+    float G[3];
+    sph16_grad_dot(g.ux, g.uy, g.uz, yb, G);
+    const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
+    if (valid && h == 0) {
+      gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
+      gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
+      gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+    }
+  }
+}
+
+constexpr int WAVES = 4;
+
+EdgeIn make_in(const ConvPlan& p, const eec_graph* g, const double* pos, Box box, double cutoff,
+               const int32_t* species, const char* ws) {
+  EdgeIn in;
+  in.pos = pos;
+  in.Lx = box.L[0];
+  in.Ly = box.L[1];
+  in.Lz = box.L[2];
+  in.rc = cutoff;
+  in.recv = (const int32_t*)(ws + p.off_recv);
+  in.col = g->col;
+  in.shift = g->shift;
+  in.species = species;
+  in.n_atoms = g->n_atoms;
+  in.n_edges = g->n_edges;
+  return in;
+}
+
+Sched make_sched(const ConvPlan& p, const char* ws, int64_t e0, int64_t e1) {
+  Sched sc;
+  sc.P = p.P;
+  sc.e0 = e0;
+  sc.e1 = e1;
+  if (p.S > 1) {
+    sc.perm = (const int32_t*)(ws + p.off_perm);
+    sc.pair_start = (const int64_t*)(ws + p.off_pair_start);
+  } else {
+    sc.perm = nullptr;
+    sc.pair_start = nullptr;
+  }
+  return sc;
+}
+
+int grid_for(const ConvPlan& p, int64_t e0, int64_t e1) {
+  const int64_t tiles = (e1 - e0 + 31) / 32 + p.P;
+  const int64_t batches = (tiles + WAVES - 1) / WAVES + p.P;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(batches, 256));
+}
+
+}  // namespace
+
+void launch_radial(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                   double cutoff, const int32_t* species, const eec_model* m, const float* basis_in,
+                   int64_t e_begin, int64_t e_end, float* R_out, float* Y_out, const char* ws) {
+  if (e_end <= e_begin) return;
+  const EdgeIn in = make_in(p, g, pos, box, cutoff, species, ws);
+  const Sched sc = make_sched(p, ws, e_begin, e_end);
+  const int grid = grid_for(p, e_begin, e_end);
+  const int64_t row_base = basis_in ? 0 : e_begin;
+  if (p.C == 64) {
+    if (basis_in)
+      k_radial<64, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, basis_in, row_base, R_out, Y_out);
+    else
+      k_radial<64, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, nullptr, row_base, R_out, Y_out);
+  } else {
+    if (basis_in)
+      k_radial<128, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, basis_in, row_base, R_out, Y_out);
+    else
+      k_radial<128, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, nullptr, row_base, R_out, Y_out);
+  }
+}
+
+void launch_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                     double cutoff, const int32_t* species, const eec_model* m, const float* Abar,
+                     float* gout, const char* ws) {
+  if (p.E == 0) return;
+  const EdgeIn in = make_in(p, g, pos, box, cutoff, species, ws);
+  const Sched sc = make_sched(p, ws, 0, p.E);
+  const int grid = grid_for(p, 0, p.E);
+  if (p.C == 64)
+    k_backward<64, WAVES><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, m->emb, p.S, Abar, gout);
+  else
+    k_backward<128, WAVES><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, m->emb, p.S, Abar, gout);
+}
+
+}  // namespace eec

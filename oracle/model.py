@@ -163,11 +163,17 @@ def _segment_sum(vals, local_recv, n_rows):
 
 
 # ------------------------------------------------------------------ forward
+def edge_messages(d, pairs, hj, model):
+    """Per-edge messages R_{e,l,c} Y_{e,lm} h_{Z_j,c} [ne, 16, C] and the stage values."""
+    st = _edge_stage(d, pairs, model, model.cutoff)
+    R = st["R"].reshape(-1, 4, model.channels)
+    return R[:, LIDX, :] * st["Y"][:, :, None] * hj[:, None, :], st
+
+
 def forward_edges(d, csr: CSR, species, model, keep_edges: bool = False):
     """A [N, 16, C], E_i [N], E from edge vectors d [E, 3] on a fixed CSR."""
     n = len(csr.row_ptr) - 1
     C = model.channels
-    rc = model.cutoff
     h = _f64(model.emb)
     w = _f64(model.w_read)
     pairs = pair_index(species, csr, model.n_species)
@@ -179,10 +185,7 @@ def forward_edges(d, csr: CSR, species, model, keep_edges: bool = False):
         e0, e1 = rp[i0], rp[i1]
         if e1 == e0:
             continue
-        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, rc)
-        R = st["R"].reshape(-1, 4, C)
-        hj = h[species[csr.col[e0:e1]]]
-        msg = R[:, LIDX, :] * st["Y"][:, :, None] * hj[:, None, :]
+        msg, st = edge_messages(d[e0:e1], pairs[e0:e1], h[species[csr.col[e0:e1]]], model)
         A[i0:i1] = _segment_sum(msg, recv[e0:e1] - i0, i1 - i0)
         if keep_edges:
             for k in ("r", "b", "Y", "R"):
@@ -196,13 +199,40 @@ def forward_edges(d, csr: CSR, species, model, keep_edges: bool = False):
 
 
 # ------------------------------------------------------------------ backward
+def edge_backward(d, pairs, hj, Ab, model):
+    """g_e = dE/dd_e [ne, 3] for edges with vectors d, pair indices, sender
+    embeddings hj [ne, C] and the receivers' dE/dA rows Ab [ne, 16, C]."""
+    C = model.channels
+    ne = len(d)
+    st = _edge_stage(d, pairs, model, model.cutoff, want_grad=True)
+    R = st["R"].reshape(ne, 4, C)
+    Y = st["Y"]
+    rho = R * hj[:, None, :]
+    Ybar = (Ab * rho[:, LIDX, :]).sum(axis=2)  # dE/dY [ne, 16]
+    Rbar = np.zeros((ne, 4, C))
+    for l in range(4):
+        ks = np.flatnonzero(LIDX == l)
+        Rbar[:, l, :] = hj * (Ab[:, ks, :] * Y[:, ks, None]).sum(axis=1)
+    Rbar = Rbar.reshape(ne, 4 * C)
+    bbar = np.zeros((ne, N_BASIS))
+    for p in np.unique(pairs):
+        sel = pairs == p
+        s2bar = Rbar[sel] @ _f64(model.W3[p]).T
+        z2bar = s2bar * silu_d(st["z2"][sel])
+        s1bar = z2bar @ _f64(model.W2[p]).T
+        z1bar = s1bar * silu_d(st["z1"][sel])
+        bbar[sel] = z1bar @ _f64(model.W1[p]).T
+    rbar = (bbar * st["db"]).sum(axis=1)
+    G = np.einsum("ek,ekx->ex", Ybar, st["dY"])
+    u = st["u"]
+    r = st["r"]
+    return rbar[:, None] * u + (G - (G * u).sum(axis=1, keepdims=True) * u) / r[:, None]
+
+
 def backward_edges(d, csr: CSR, species, model, A):
     """g_e = dE/dd_e [E, 3] given the complete per-atom A."""
-    C = model.channels
-    rc = model.cutoff
     h = _f64(model.emb)
-    w = _f64(model.w_read)
-    Abar = 2.0 * w[None, None, :] * A  # dE/dA
+    Abar = 2.0 * _f64(model.w_read)[None, None, :] * A  # dE/dA
     pairs = pair_index(species, csr, model.n_species)
     recv = csr.receivers()
     g = np.zeros((csr.n_edges, 3))
@@ -211,33 +241,8 @@ def backward_edges(d, csr: CSR, species, model, A):
         e0, e1 = rp[i0], rp[i1]
         if e1 == e0:
             continue
-        st = _edge_stage(d[e0:e1], pairs[e0:e1], model, rc, want_grad=True)
-        ne = e1 - e0
-        R = st["R"].reshape(ne, 4, C)
-        Y = st["Y"]
-        hj = h[species[csr.col[e0:e1]]]
-        Ab = Abar[recv[e0:e1]]  # [ne, 16, C]
-        rho = R * hj[:, None, :]
-        Ybar = (Ab * rho[:, LIDX, :]).sum(axis=2)  # dE/dY [ne, 16]
-        Rbar = np.zeros((ne, 4, C))
-        for l in range(4):
-            ks = np.flatnonzero(LIDX == l)
-            Rbar[:, l, :] = hj * (Ab[:, ks, :] * Y[:, ks, None]).sum(axis=1)
-        Rbar = Rbar.reshape(ne, 4 * C)
-        bbar = np.zeros((ne, N_BASIS))
-        pp = pairs[e0:e1]
-        for p in np.unique(pp):
-            sel = pp == p
-            s2bar = Rbar[sel] @ _f64(model.W3[p]).T
-            z2bar = s2bar * silu_d(st["z2"][sel])
-            s1bar = z2bar @ _f64(model.W2[p]).T
-            z1bar = s1bar * silu_d(st["z1"][sel])
-            bbar[sel] = z1bar @ _f64(model.W1[p]).T
-        rbar = (bbar * st["db"]).sum(axis=1)
-        G = np.einsum("ek,ekx->ex", Ybar, st["dY"])
-        u = st["u"]
-        r = st["r"]
-        g[e0:e1] = rbar[:, None] * u + (G - (G * u).sum(axis=1, keepdims=True) * u) / r[:, None]
+        g[e0:e1] = edge_backward(d[e0:e1], pairs[e0:e1], h[species[csr.col[e0:e1]]],
+                                 Abar[recv[e0:e1]], model)
     return g
 
 

@@ -1,0 +1,101 @@
+"""Energy, forces, virial and the streaming message against the float64 oracle.
+
+Tolerances: energy within 1e-5 relative; forces max|dF| <= 1e-4 RMS(F);
+every output finite.  The message A is compared to 2e-5 of its largest
+magnitude (float32 sums of <= 158 products of O(1) terms)."""
+import numpy as np
+import pytest
+import torch
+
+import eec_inputs as I
+from equivariant_edge_convolution_amd import binding as B
+from oracle import model as M
+from oracle import neighbors as N
+from oracle.sampled import sampled_energy_forces
+
+from gpu_util import device_inputs, graph_for, np_, rms, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["D64", "RS2", "RS3", "PV2", "PV3", "D64c128", "D512", "D512c128"]
+
+
+def _run(name, virial=False):
+    cfg = I.make_config(name)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    out = B.energy_forces(g, pos, cfg.box, species, model, virial=virial)
+    return cfg, pos, species, model, g, {k: np_(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_energy_forces_elementwise(name):
+    say(f"[energy_forces] {name}")
+    cfg, *_, got = _run(name, virial=True)
+    ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
+    for k in ("energy", "atom_energy", "forces", "virial"):
+        assert np.all(np.isfinite(got[k])), k
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    F0 = ref["F"]
+    assert np.abs(got["forces"] - F0).max() <= 1e-4 * rms(F0)
+    W0 = ref["virial"]
+    assert np.abs(got["virial"] - W0).max() <= 1e-4 * np.abs(W0).max()
+
+
+@pytest.mark.parametrize("name", ["D64", "PV3", "D512", "D64c128"])
+def test_edge_message(name):
+    say(f"[edge_message] {name}")
+    cfg = I.make_config(name)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    A = np_(B.edge_message(g, pos, cfg.box, species, model))
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    A0 = M.forward_edges(N.edge_vectors(cfg.pos, cfg.box, csr), csr, cfg.species, cfg.model)["A"]
+    assert np.all(np.isfinite(A))
+    assert np.abs(A - A0).max() <= 2e-5 * np.abs(A0).max()
+
+
+@pytest.mark.parametrize("name,n_e,n_f", [("D4096", 256, 3), ("RS", 256, 6), ("PV", 256, 4), ("D32k", 96, 2)])
+def test_full_size_sampled(name, n_e, n_f):
+    """Full-size cells in the benchmark's launch configuration; exact per-atom
+    energies and forces of sampled atoms from the oracle."""
+    say(f"[full-size] {name}")
+    cfg, pos, species, model, g, got = _run(name)
+    for k in ("energy", "atom_energy", "forces"):
+        assert np.all(np.isfinite(got[k])), k
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    rng = np.random.default_rng(123)
+    atoms = np.sort(rng.choice(cfg.n_atoms, n_e, replace=False))
+    fat = atoms[:n_f]
+    ref = sampled_energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, csr, atoms, forces_for=fat)
+    ei = got["atom_energy"][ref["atoms"]]
+    assert np.abs(ei - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    # the force scale: RMS over all atoms of the GPU forces (an estimate of RMS(F))
+    Fs = rms(got["forces"])
+    assert np.abs(got["forces"][ref["force_atoms"]] - ref["F"]).max() <= 1e-4 * Fs
+    # total = float64 sum of the per-atom energies
+    tot = float(np.sum(got["atom_energy"].astype(np.float64)))
+    assert abs(float(got["energy"][0]) - tot) <= 1e-6 * np.abs(got["atom_energy"]).sum()
+    assert np.abs(got["forces"].astype(np.float64).sum(axis=0)).max() <= 1e-5 * np.abs(got["forces"]).sum()
+
+
+def test_full_energy_headline_cell():
+    """Total energy of the 4096-atom diamond against the full oracle forward."""
+    say("[full-size] D4096 total energy")
+    cfg, *_, got = _run("D4096")
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    E0 = M.forward_edges(N.edge_vectors(cfg.pos, cfg.box, csr), csr, cfg.species, cfg.model)["E"]
+    assert abs(float(got["energy"][0]) - E0) <= 1e-5 * abs(E0)
+
+
+def test_bitwise_repeatable():
+    cfg = I.make_config("PV3")
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    ef = B.EnergyForces(g, model, pos.device, virial=True)
+    ef(pos, cfg.box, species)
+    E, F, W = ef.energy.clone(), ef.forces.clone(), ef.virial.clone()
+    for _ in range(20):
+        ef(pos, cfg.box, species)
+        assert torch.equal(ef.energy, E) and torch.equal(ef.forces, F) and torch.equal(ef.virial, W)
