@@ -265,14 +265,20 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   launch_prepare(s, p, g, species, ws, A);
   mark(2 * EEC_PHASE_PREPARE + 1);
   mark(2 * EEC_PHASE_FORWARD);
-  for (int64_t e0 = 0; e0 < p.E; e0 += p.chunk) {
-    const int64_t e1 = std::min<int64_t>(p.E, e0 + p.chunk);
-    launch_radial(s, p, g, pos, b, m->cutoff, species, m, nullptr, e0, e1, Rc, Yc, ws);
-    launch_message(s, p, g, species, m, e0, e1, Rc, Yc, A, ws);
+  int nparts = 1;
+  if (fused_forward_supported(p)) {
+    launch_forward(s, p, g, pos, b, m->cutoff, species, m, A, ws);  // S partial slabs
+    nparts = p.S;
+  } else {
+    for (int64_t e0 = 0; e0 < p.E; e0 += p.chunk) {
+      const int64_t e1 = std::min<int64_t>(p.E, e0 + p.chunk);
+      launch_radial(s, p, g, pos, b, m->cutoff, species, m, nullptr, e0, e1, Rc, Yc, ws);
+      launch_message(s, p, g, species, m, e0, e1, Rc, Yc, A, ws);
+    }
   }
   mark(2 * EEC_PHASE_FORWARD + 1);
   mark(2 * EEC_PHASE_READOUT);
-  launch_readout(s, p, m, A, ei, nullptr, energy);  // A now holds dE/dA
+  launch_readout(s, p, m, A, nparts, ei, energy);  // slab 0 of A now holds dE/dA
   mark(2 * EEC_PHASE_READOUT + 1);
   float* gbuf = (float*)(ws + p.off_g);
   mark(2 * EEC_PHASE_BACKWARD);

@@ -133,53 +133,91 @@ __global__ void __launch_bounds__(256) k_pair_scatter(int64_t E, const int32_t* 
   }
 }
 
+// Position range, in the pair-grouped order, of the edges of receiver i whose
+// sender has species s: inside the group of pair (Z_i, s) the CSR indices
+// ascend, so the range is [lower_bound(row_ptr[i]), lower_bound(row_ptr[i+1])).
+__global__ void __launch_bounds__(256) k_seg_bounds(int32_t n, int S, const int32_t* __restrict__ rp,
+                                                    const int32_t* __restrict__ species,
+                                                    const int64_t* __restrict__ pair_start,
+                                                    const int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ seg) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)n * S) return;
+  const int s = (int)(t / n), i = (int)(t % n);
+  const int zi = min(max(species[i], 0), S - 1);
+  const int p = zi * S + s;
+  int64_t lo = pair_start[p], hi = pair_start[p + 1];
+  const int64_t g1 = hi;
+  const int64_t a = rp[i], b = rp[i + 1];
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)perm[mid] < a) lo = mid + 1; else hi = mid;
+  }
+  int64_t lo2 = lo, hi2 = g1;
+  while (lo2 < hi2) {
+    const int64_t mid = (lo2 + hi2) >> 1;
+    if ((int64_t)perm[mid] < b) lo2 = mid + 1; else hi2 = mid;
+  }
+  seg[2 * t] = (int32_t)lo;
+  seg[2 * t + 1] = (int32_t)lo2;
+}
+
 // ------------------------------------------------------------ message
 // One workgroup of 4 waves per receiver; lanes over channels; each wave sums a
-// contiguous quarter of the receiver's edges inside the chunk in CSR order, and
-// the quarters are added in a fixed order.
+// contiguous quarter of the receiver's edges inside the chunk in CSR order
+// (four edges per step, all loads first), and the quarters are added in a
+// fixed order.  The chunk rows already hold rho = R h_{Z_j}.
 template <int C>
 __global__ void __launch_bounds__(256) k_message(int64_t e0, int64_t e1, const int32_t* __restrict__ rp,
                                                  const int32_t* __restrict__ recv,
-                                                 const int32_t* __restrict__ col,
-                                                 const int32_t* __restrict__ species,
-                                                 const float* __restrict__ emb, int S, int n,
                                                  const float* __restrict__ Rc,
                                                  const float* __restrict__ Yc, float* __restrict__ A) {
   constexpr int CPL = C / 64;  // channels per lane
   constexpr int NC = 4 * C;
+  constexpr int U = 4;         // edges in flight per wave
   __shared__ float part[3][NLM * C];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i_first = recv[e0], i_last = recv[e1 - 1];
   for (int i = i_first + blockIdx.x; i <= i_last; i += gridDim.x) {
     const int64_t ra = std::max<int64_t>(rp[i], e0), rb = std::min<int64_t>(rp[i + 1], e1);
     const int64_t len = rb - ra, per = (len + 3) / 4;
-    const int64_t wa = std::min(rb, ra + wave * per), wb = std::min(rb, wa + per);
+    const int wa = (int)(std::min(rb, ra + wave * per) - e0);
+    const int wb = (int)(std::min<int64_t>(rb, ra + (wave + 1) * per) - e0);
     float acc[CPL][NLM];
 #pragma unroll
     for (int q = 0; q < CPL; ++q)
 #pragma unroll
       for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
-    for (int64_t e = wa; e < wb; ++e) {
-      const int64_t el = __builtin_amdgcn_readfirstlane((int)(e - e0));
-      const int j = min(max(col[e0 + el], 0), n - 1);
-      const int zj = min(max(species[j], 0), S - 1);
-      const float* yr = Yc + el * NLM;
-      const float* rr = Rc + el * NC;
-      float y[NLM];
+    int el = __builtin_amdgcn_readfirstlane(wa);
+    for (; el < wb; el += U) {
+      float rv[U][CPL][4];
+      float y[U][NLM];
 #pragma unroll
-      for (int k = 0; k < NLM; ++k) y[k] = yr[k];
+      for (int u = 0; u < U; ++u) {
+        const int eu = min(el + u, wb - 1);  // in-range duplicate for the tail; weighted 0 below
+        const float* rr = Rc + (size_t)eu * NC;
+        const float* yr = Yc + (size_t)eu * NLM;
 #pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const int c = lane + 64 * q;
-        const float hc = emb[zj * C + c];
-        const float r0 = rr[c] * hc, r1 = rr[C + c] * hc, r2 = rr[2 * C + c] * hc, r3 = rr[3 * C + c] * hc;
-        acc[q][0] += r0 * y[0];
+        for (int q = 0; q < CPL; ++q)
 #pragma unroll
-        for (int k = 1; k < 4; ++k) acc[q][k] += r1 * y[k];
+          for (int l = 0; l < 4; ++l) rv[u][q][l] = rr[l * C + lane + 64 * q];
 #pragma unroll
-        for (int k = 4; k < 9; ++k) acc[q][k] += r2 * y[k];
+        for (int k = 0; k < NLM; ++k) y[u][k] = yr[k];
+      }
 #pragma unroll
-        for (int k = 9; k < 16; ++k) acc[q][k] += r3 * y[k];
+      for (int u = 0; u < U; ++u) {
+        if (el + u < wb) {
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            acc[q][0] += rv[u][q][0] * y[u][0];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) acc[q][k] += rv[u][q][1] * y[u][k];
+#pragma unroll
+            for (int k = 4; k < 9; ++k) acc[q][k] += rv[u][q][2] * y[u][k];
+#pragma unroll
+            for (int k = 9; k < 16; ++k) acc[q][k] += rv[u][q][3] * y[u][k];
+          }
+        }
       }
     }
     if (wave > 0) {
@@ -206,16 +244,18 @@ __global__ void __launch_bounds__(256) k_message(int64_t e0, int64_t e1, const i
 }
 
 // ------------------------------------------------------------ readout
-// One wave per atom: E_i = sum_c w_c sum_lm A^2 (fixed lane order and shuffle
-// tree), Abar = 2 w A written over A.
+// One wave per atom: A = sum over the partial slabs in slab order, E_i =
+// sum_c w_c sum_lm A^2 (fixed lane order and shuffle tree), and dE/dA = 2 w A
+// written over slab 0.
 template <int C>
-__global__ void __launch_bounds__(256) k_readout(int32_t n, const float* __restrict__ w,
+__global__ void __launch_bounds__(256) k_readout(int32_t n, int nparts, const float* __restrict__ w,
                                                  float* __restrict__ A, float* __restrict__ ei) {
   constexpr int CPL = C / 64;
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
   float* ai = A + (size_t)i * NLM * C;
+  const size_t slab = (size_t)n * NLM * C;
   float sum = 0.f;
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
@@ -224,7 +264,8 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, const float* __restr
     float s2 = 0.f;
 #pragma unroll
     for (int k = 0; k < NLM; ++k) {
-      const float a = ai[k * C + c];
+      float a = ai[k * C + c];
+      for (int pt = 1; pt < nparts; ++pt) a += ai[pt * slab + k * C + c];
       s2 += a * a;
       ai[k * C + c] = 2.f * wc * a;
     }
@@ -390,8 +431,9 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
     p.off_perm = o;       o += align256(4 * (size_t)E);
     p.off_pair_start = o; o += align256(8 * (size_t)(p.P + 1));
     p.off_blockcnt = o;   o += align256((4 + 8) * (size_t)p.P * std::max<int64_t>(p.n_count_blocks, 1));
+    p.off_seg = o;        o += align256(8 * (size_t)p.S * N);
   }
-  p.off_A = o;     o += align256(4 * (size_t)N * NLM * p.C);
+  p.off_A = o;     o += align256(4 * (size_t)p.S * N * NLM * p.C);  // S partial slabs
   p.off_R = o;     o += align256(4 * (size_t)p.chunk * p.NC);
   p.off_Y = o;     o += align256(4 * (size_t)p.chunk * NLM);
   p.off_g = o;     o += align256(4 * 3 * (size_t)E);
@@ -417,6 +459,10 @@ void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
     k_pair_count<<<(int)nb, 256, 0, s>>>(p.E, recv, g->col, species, p.S, p.N, nb, cnt);
     k_pair_scan<<<1, 1024, 0, s>>>(nb, p.P, cnt, off, pair_start, p.E);
     k_pair_scatter<<<(int)nb, 256, 0, s>>>(p.E, recv, g->col, species, p.S, p.N, nb, off, perm);
+    if (p.N > 0)
+      k_seg_bounds<<<blocks_for((int64_t)p.N * p.S, 256), 256, 0, s>>>(p.N, p.S, g->row_ptr, species,
+                                                                       pair_start, perm,
+                                                                       (int32_t*)(ws + p.off_seg));
   }
 }
 
@@ -427,20 +473,18 @@ void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
   const int32_t* recv = (const int32_t*)(ws + p.off_recv);
   const int grid = (int)std::min<int64_t>(p.N, 2048);
   if (p.C == 64)
-    k_message<64><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, g->col, species, m->emb, p.S, p.N,
-                                        R_chunk, Y_chunk, A);
+    k_message<64><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, R_chunk, Y_chunk, A);
   else
-    k_message<128><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, g->col, species, m->emb, p.S, p.N,
-                                         R_chunk, Y_chunk, A);
+    k_message<128><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, R_chunk, Y_chunk, A);
 }
 
-void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, float* ei,
-                    double*, float* energy) {
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts,
+                    float* ei, float* energy) {
   if (p.N > 0) {
     if (p.C == 64)
-      k_readout<64><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, m->w_read, A, ei);
+      k_readout<64><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
     else
-      k_readout<128><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, m->w_read, A, ei);
+      k_readout<128><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
   }
   k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
 }

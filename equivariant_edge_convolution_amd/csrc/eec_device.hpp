@@ -97,13 +97,15 @@ __device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16]
   const double env = envelope(x);
   const double inv_r = 1.0 / r;
   const double envd = DERIV ? envelope_d(x) / rc : 0.0;
+  const double kstep = PI / rc;
+  double kn = (double)n0 * kstep;  // n pi / rc, advanced with n
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const double sr = s * inv_r;
     b[k] = (float)(sr * env);
     if (DERIV) {
-      const double kn = (double)(n0 + k) * (PI / rc);
       db[k] = (float)((kn * c * inv_r - sr * inv_r) * env + sr * envd);
+      kn += kstep;
     }
     const double sn = s * c1 + c * s1;
     const double cn = c * c1 - s * s1;

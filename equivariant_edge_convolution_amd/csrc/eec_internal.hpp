@@ -43,8 +43,8 @@ struct ConvPlan {
   int32_t N;
   int64_t chunk;  // edges per streamed chunk
   size_t bytes;
-  size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_A, off_R, off_Y, off_g, off_epart,
-      off_vpart, off_ei;
+  size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_seg, off_A, off_R, off_Y, off_g,
+      off_epart, off_vpart, off_ei;
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
@@ -66,9 +66,18 @@ void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
                     const eec_model* m, int64_t e_begin, int64_t e_end, const float* R_chunk,
                     const float* Y_chunk, float* A, const char* ws);
 
-// Readout: E_i (into ei), per-block energy partials, Abar = 2 w A in place.
-void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, float* ei,
-                    double* epart, float* energy);
+// Readout: A_i = sum of `nparts` partial slabs [nparts][N][16][C] (fixed order),
+// E_i (into ei), the total energy, and dE/dA = 2 w A written over slab 0.
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts,
+                    float* ei, float* energy);
+
+// Fused forward (C = 64): radial network + message per (pair, receiver) unit,
+// writing the S partial A slabs.  The chunked path (launch_radial +
+// launch_message) covers every supported shape.
+bool fused_forward_supported(const ConvPlan& p);
+void launch_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                    double cutoff, const int32_t* species, const eec_model* m, float* A_out,
+                    const char* ws);
 
 // Backward over all edges: g = dE/dd.
 void launch_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

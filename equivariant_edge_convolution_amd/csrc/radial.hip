@@ -187,11 +187,15 @@ __device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) {
 }
 
 // ------------------------------------------------------------------ forward
+// With `emb` non-NULL the rows written are rho = R h_{Z_j} (the sender embedding
+// folded into the streamed chunk, which the message pass then only sums);
+// otherwise plain R.
 template <int C, int W, bool BASIS_IN>
 __global__ void __launch_bounds__(64 * W)
 k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restrict__ W2,
-         const float* __restrict__ W3, const float* __restrict__ basis_in, int64_t row_base,
-         float* __restrict__ R_out, float* __restrict__ Y_out) {
+         const float* __restrict__ W3, const float* __restrict__ emb, int n_species,
+         const float* __restrict__ basis_in, int64_t row_base, float* __restrict__ R_out,
+         float* __restrict__ Y_out) {
   constexpr int NC = Lds<C>::NC;
   __shared__ float lds[Lds<C>::FLOATS];
   __shared__ SchedState st;
@@ -249,15 +253,148 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
     // R = s2 W3 with edges on M: D[edge][feature], lane = feature 32 t + s.
     constexpr int LD3 = Lds<C>::LD3;
     const float* w3 = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
+    const float* hrow = emb ? emb + (size_t)(p % n_species) * C : nullptr;
 #pragma unroll 1
     for (int t = 0; t < NC / 32; ++t, w3 += 32) {
       f32x16 acc = zero16();
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks) acc = mfma32(a[ks >> 4][ks & 15], w3[hid_k0(ks) * LD3], acc);
+      if (hrow) {
+        const float hc = hrow[(32 * t + s) % C];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] *= hc;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (orow[r] >= 0) R_out[(size_t)orow[r] * NC + 32 * t + s] = acc[r];
     }
+  }
+}
+
+// ------------------------------------------------------------------ fused forward
+// One wave per (ordered species pair, receiver) unit: the receiver's edges of
+// that pair, in 32-edge tiles aligned to the receiver, through geometry ->
+// basis -> z1 -> z2 (edges on N) -> rho = (s2 W3) h (edges on M: the lane owns
+// one channel column of 16 edges) and the message accumulated in registers:
+// A_{i,lm,c} += rho_{e,l,c} Y_{e,lm}, in a fixed order.  Each lane half sums its
+// own 16 edge rows of every tile; the halves are added at the end.  The tile's
+// harmonics go through a per-wave LDS slot (rows of padding edges are zero).
+// No radial row ever leaves the chip.  Output: the unit's partial A (sender
+// species s) at A_out + (s * N + i) * 16 * C.
+struct Units {
+  const int32_t* row_ptr;
+  const int32_t* species;
+  const int32_t* perm;   // pair-grouped order -> CSR edge (S > 1); NULL when S == 1
+  const int32_t* seg;    // [S][N][2] position range of unit (i, s) in that order (S > 1)
+  int32_t n_atoms;
+  int S;
+};
+
+template <int W>
+__global__ void __launch_bounds__(64 * W)
+k_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
+          const float* __restrict__ W3, const float* __restrict__ emb, float* __restrict__ A_out) {
+  constexpr int C = 64, NC = 256;
+  constexpr int LD3 = Lds<C>::LD3;
+  __shared__ float lds[Lds<C>::FLOATS];
+  __shared__ float ysm[W][32][NLM + 1];  // one padding column against bank conflicts
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = lane & 31, h = lane >> 5;
+  const float* w1s = lds + Lds<C>::W1;
+  const float* w2s = lds + Lds<C>::W2;
+  const float* w3s = lds + Lds<C>::W3;
+  const int N = un.n_atoms, S = un.S, P = S * S;
+  const int nbp = (N + W - 1) / W;  // batches of W receivers per pair
+  int loaded = -1;
+  for (int b = blockIdx.x; b < P * nbp; b += gridDim.x) {
+    const int p = b / nbp;
+    if (p != loaded) {
+      __syncthreads();
+      stage_weights<C>(lds, W1, W2, W3, p);
+      __syncthreads();
+      loaded = p;
+    }
+    const int i = (b - p * nbp) * W + wave;
+    if (i >= N) continue;
+    const int zs = p % S;
+    int qa, qb;
+    if (S == 1) {
+      qa = un.row_ptr[i];
+      qb = un.row_ptr[i + 1];
+    } else {
+      if (min(max(un.species[i], 0), S - 1) != p / S) continue;  // another pair's receiver
+      qa = un.seg[2 * ((size_t)zs * N + i)];
+      qb = un.seg[2 * ((size_t)zs * N + i) + 1];
+    }
+    const float* hrow = emb + (size_t)zs * C;
+    const float h0 = hrow[s], h1 = hrow[32 + s];  // channel of tiles with t even / odd
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+
+    for (int q0 = qa; q0 < qb; q0 += 32) {
+      const int q = q0 + s;
+      const bool valid = q < qb;
+      const int qq = valid ? q : qa;
+      const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
+      const Geo g = edge_geo(in, e);
+      f32x16 z[2], a[2];
+      {
+        float bas[16];
+        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+        layer1(w1s, bas, s, h, z);
+      }
+      silu_tiles(z, a);
+      layer2(w2s, a, s, h, z);
+      silu_tiles(z, a);  // a = s2; as the A operand: row = edge slot s
+      {
+        float Y[16];
+        sph16(g.ux, g.uy, g.uz, Y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ysm[wave][s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float* w3 = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        // the two 32-channel tiles of degree l: t = 2 l (channel s) and 2 l + 1 (32 + s)
+        f32x16 r0 = zero16(), r1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const float av = a[ks >> 4][ks & 15];
+          r0 = mfma32(av, w3[hid_k0(ks) * LD3 + 64 * l], r0);
+          r1 = mfma32(av, w3[hid_k0(ks) * LD3 + 64 * l + 32], r1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int off[4] = {0, 2, 8, 18};  // acc offset of (l, tile 2l); tile 2l+1 follows
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float* yr = &ysm[wave][fperm(r) + 4 * h][l * l];
+          const float p0 = r0[r] * h0, p1 = r1[r] * h1;
+#pragma unroll
+          for (int m = 0; m < 2 * l + 1; ++m) {
+            const float y = yr[m];
+            acc[off[l] + m] += p0 * y;
+            acc[off[l] + 2 * l + 1 + m] += p1 * y;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    // add the two lane halves' edge subsets; half 0 writes the even tiles, half 1 the odd
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] += __shfl_xor(acc[k], 32);
+    float* ai = A_out + ((size_t)zs * N + i) * NLM * C + 32 * h + s;
+    constexpr int off[4] = {0, 2, 8, 18};
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
+#pragma unroll
+      for (int m = 0; m < 2 * l + 1; ++m)
+        ai[(l * l + m) * C] = h == 0 ? acc[off[l] + m] : acc[off[l] + 2 * l + 1 + m];
   }
 }
 
@@ -296,15 +433,17 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     const int zj = p % n_species;
 
     const Geo g = edge_geo(in, e);
-    float bas[16], dbas[16], Y[16];
-    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
-    sph16(g.ux, g.uy, g.uz, Y);
-
     f32x16 z[2], a[2];
-    layer1(w1s, bas, s, h, z);
+    {
+      float bas[16];
+      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+      layer1(w1s, bas, s, h, z);
+    }
     silu_tiles(z, a);
     layer2(w2s, a, s, h, z);
     silu_tiles(z, a);  // a = s2
+    float Y[16];
+    sph16(g.ux, g.uy, g.uz, Y);
 
     const float* abar = Abar + (size_t)g.i * NLM * C;
     const float* hrow = emb + (size_t)zj * C;
@@ -316,67 +455,83 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     for (int k = 0; k < 16; ++k) ybp[k] = 0.f;
 
     constexpr int LD3 = Lds<C>::LD3;
-    const float* w3r = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
-    const float* w3c = w3s + s * LD3 + 4 * h;  // W3[32 m + s][32 t + fperm(ks) + 4 h]
+    constexpr int TPL = C / 32;  // 32-feature tiles per degree
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const float* w3r = w3s + 4 * h * LD3 + s + 32 * TPL * l;  // W3[hid_k0(ks) + 4 h][32 t + s]
+      const float* w3c = w3s + s * LD3 + 4 * h + 32 * TPL * l;  // W3[32 m + s][32 t + fperm(ks) + 4 h]
 #pragma unroll 1
-    for (int t = 0; t < NC / 32; ++t, w3r += 32, w3c += 32) {
-      // R tile (edges on N): register r = feature 32 t + fperm(r) + 4h of edge s
-      f32x16 acc = zero16();
+      for (int tc = 0; tc < TPL; ++tc, w3r += 32, w3c += 32) {
+        // R tile (edges on N): register r = feature (l, c = 32 tc + fperm(r) + 4h) of edge s
+        f32x16 acc = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 32; ++ks) acc = mfma32(w3r[hid_k0(ks) * LD3], a[ks >> 4][ks & 15], acc);
-      const int ldeg = (32 * t) / C;
-      const int cb = (32 * t) % C + 4 * h;
-      float hv[16], rb[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v = *reinterpret_cast<const float4*>(hrow + cb + 8 * q4);
-        hv[4 * q4 + 0] = v.x; hv[4 * q4 + 1] = v.y; hv[4 * q4 + 2] = v.z; hv[4 * q4 + 3] = v.w;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[r] *= hv[r];  // rho = R h
-        rb[r] = 0.f;
-      }
-      const int lm0 = ldeg * ldeg;
-      for (int mm = 0; mm < 2 * ldeg + 1; ++mm) {
-        const int lm = lm0 + mm;
-        const float* ar = abar + lm * C + cb;
-        float av[16];
+        for (int ks = 0; ks < 32; ++ks) acc = mfma32(w3r[hid_k0(ks) * LD3], a[ks >> 4][ks & 15], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const int cb = 32 * tc + 4 * h;
+        float hv[16], rb[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v = *reinterpret_cast<const float4*>(ar + 8 * q4);
-          av[4 * q4 + 0] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
+          const float4 v = *reinterpret_cast<const float4*>(hrow + cb + 8 * q4);
+          hv[4 * q4 + 0] = v.x; hv[4 * q4 + 1] = v.y; hv[4 * q4 + 2] = v.z; hv[4 * q4 + 3] = v.w;
         }
-        float yb = 0.f;
-        const float ylm = Y[lm];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          yb += av[r] * acc[r];
-          rb[r] += av[r] * ylm;
+          acc[r] *= hv[r];  // rho = R h
+          rb[r] = 0.f;
         }
-        ybp[lm] += yb;
+#pragma unroll
+        for (int lm = l * l; lm < (l + 1) * (l + 1); ++lm) {
+          const float* ar = abar + lm * C + cb;
+          float av[16];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = *reinterpret_cast<const float4*>(ar + 8 * q4);
+            av[4 * q4 + 0] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
+          }
+          float yb = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            yb += av[r] * acc[r];
+            rb[r] += av[r] * Y[lm];
+          }
+          ybp[lm] += yb;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rb[r] *= hv[r];
+        __builtin_amdgcn_sched_barrier(0);
+        // s2bar += W3[:, tile] Rbar_tile (edges on N)
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) sb[m] = mfma32(w3c[32 * m * LD3 + fperm(ks)], rb[ks], sb[m]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rb[r] *= hv[r];
-      // s2bar += W3[:, tile t] Rbar_t (edges on N)
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) sb[m] = mfma32(w3c[32 * m * LD3 + fperm(ks)], rb[ks], sb[m]);
     }
-    float yb[16];
+    // Ybar (both lane halves hold partial sums over their channels) and its
+    // contraction with the harmonic gradients, G = sum_lm Ybar_lm grad Y_lm
+    float G[3];
+    {
+      float yb[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) yb[k] = ybp[k] + __shfl_xor(ybp[k], 32);
+      for (int k = 0; k < 16; ++k) yb[k] = ybp[k] + __shfl_xor(ybp[k], 32);
+      sph16_grad_dot(g.ux, g.uy, g.uz, yb, G);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // recompute z1, z2 (fewer live registers through the loop above)
+    // recompute the basis (with its r-derivative), z1 and z2: nothing of the
+    // forward stays live through the loop above
+    float bas[16], dbas[16];
+    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
     f32x16 z1[2], s1[2];
     layer1(w1s, bas, s, h, z1);
     silu_tiles(z1, s1);
     layer2(w2s, s1, s, h, z);  // z = z2
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sb[m][r] *= silu_d(z[m][r]);  // z2bar
+    __builtin_amdgcn_sched_barrier(0);
     // s1bar = z2bar W2^T
     f32x16 s1b[2];
     s1b[0] = zero16();
@@ -402,8 +557,6 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
     rbar += __shfl_xor(rbar, 32);
 
-    float G[3];
-    sph16_grad_dot(g.ux, g.uy, g.uz, yb, G);
     const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
     if (valid && h == 0) {
       gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
@@ -413,7 +566,7 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
   }
 }
 
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 
 EdgeIn make_in(const ConvPlan& p, const eec_graph* g, const double* pos, Box box, double cutoff,
                const int32_t* species, const char* ws) {
@@ -462,18 +615,40 @@ void launch_radial(hipStream_t s, const ConvPlan& p, const eec_graph* g, const d
   const EdgeIn in = make_in(p, g, pos, box, cutoff, species, ws);
   const Sched sc = make_sched(p, ws, e_begin, e_end);
   const int grid = grid_for(p, e_begin, e_end);
+  // materialising mode (a given basis) writes R rows at edge index; streaming
+  // mode writes rho = R h rows of the chunk [e_begin, e_end) and its harmonics
   const int64_t row_base = basis_in ? 0 : e_begin;
+  const float* emb = basis_in ? nullptr : m->emb;
   if (p.C == 64) {
     if (basis_in)
-      k_radial<64, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, basis_in, row_base, R_out, Y_out);
+      k_radial<64, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, emb, p.S, basis_in, row_base, R_out, Y_out);
     else
-      k_radial<64, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, nullptr, row_base, R_out, Y_out);
+      k_radial<64, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, emb, p.S, nullptr, row_base, R_out, Y_out);
   } else {
     if (basis_in)
-      k_radial<128, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, basis_in, row_base, R_out, Y_out);
+      k_radial<128, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, emb, p.S, basis_in, row_base, R_out, Y_out);
     else
-      k_radial<128, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, nullptr, row_base, R_out, Y_out);
+      k_radial<128, WAVES, false><<<grid, 64 * WAVES, 0, s>>>(in, sc, m->W1, m->W2, m->W3, emb, p.S, nullptr, row_base, R_out, Y_out);
   }
+}
+
+bool fused_forward_supported(const ConvPlan& p) { return p.C == 64; }
+
+void launch_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                    double cutoff, const int32_t* species, const eec_model* m, float* A_out,
+                    const char* ws) {
+  if (p.N == 0) return;
+  const EdgeIn in = make_in(p, g, pos, box, cutoff, species, ws);
+  Units un;
+  un.row_ptr = g->row_ptr;
+  un.species = species;
+  un.perm = p.S > 1 ? (const int32_t*)(ws + p.off_perm) : nullptr;
+  un.seg = p.S > 1 ? (const int32_t*)(ws + p.off_seg) : nullptr;
+  un.n_atoms = p.N;
+  un.S = p.S;
+  const int64_t batches = (int64_t)p.P * ((p.N + WAVES - 1) / WAVES);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(batches, 256));
+  k_forward<WAVES><<<grid, 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, m->emb, A_out);
 }
 
 void launch_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
