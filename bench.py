@@ -17,7 +17,7 @@ Also reported:
                 (network input gradient 45,056 + Rbar 2,304 + Ybar 2,048)
                 over that duration, against the FP32 matrix peak;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
-                (the first 1024 receivers: their forward and force backward),
+                (all receivers of the cell: their forward and force backward),
                 on the host cores.
 """
 from __future__ import annotations
@@ -47,7 +47,7 @@ WORKLOADS = {
 }
 
 
-def cpu_baseline(cfg, n_rows: int = 1024):
+def cpu_baseline(cfg, n_rows: int = 1 << 30):
     """The oracle (as it stands) on the first n_rows receivers of the workload."""
     import numpy as np
 
@@ -78,6 +78,43 @@ def cpu_baseline(cfg, n_rows: int = 1024):
                       f"(basis, network, harmonics, message) and force backward; {dt:.2f} s"}
 
 
+def copy_calibration(args, torch, dev) -> int:
+    """A plain device-to-device copy of 256 MiB: 256 MiB read and 256 MiB
+    written per launch, to scale the profiler's FETCH_SIZE / WRITE_SIZE."""
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "ms": dt * 1e3,
+                      "GBps": 2 * n / dt / 1e9}), flush=True)
+    return 0
+
+
+def message_mode(args, B, torch, cfg, g, pos, species, model, dev) -> int:
+    """Time eec_edge_message: radial rows streamed chunk by chunk into the
+    message pass (profile it to read the message kernel's own duration)."""
+    ws = torch.empty(B.workspace_bytes(g.n_atoms, g.n_edges, model), dtype=torch.uint8, device=dev)
+    A = torch.empty((g.n_atoms, 16, model.channels), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        B.edge_message(g, pos, cfg.box, species, model, workspace=ws, out=A)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        B.edge_message(g, pos, cfg.box, species, model, workspace=ws, out=A)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    print(json.dumps({"mode": "edge_message", "config": args.config, "n_edges": g.n_edges,
+                      "ms_per_call": ms, "edges_per_s": g.n_edges / (ms * 1e-3)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +122,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy"],
+                    help="energy_forces: the headline call; edge_message: the chunked streaming "
+                         "forward (radial rows + message pass), for profiling its kernels; copy: a "
+                         "plain 256 MiB device copy, the calibration of the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -98,6 +139,8 @@ def main() -> int:
     from equivariant_edge_convolution_amd import binding as B
 
     dev = torch.device("cuda:0")
+    if args.mode == "copy":
+        return copy_calibration(args, torch, dev)
     cfg = I.make_config(args.config)
     pos = torch.as_tensor(cfg.pos).to(dev)
     species = torch.as_tensor(cfg.species).to(dev)
@@ -111,6 +154,8 @@ def main() -> int:
     nb_ms = (time.perf_counter() - t0) * 1e3
     E = g.n_edges
 
+    if args.mode == "edge_message":
+        return message_mode(args, B, torch, cfg, g, pos, species, model, dev)
     ef = B.EnergyForces(g, model, dev, atom_energy=True)
     nph = len(B.PHASES)
     ev = B.HipEvents(2 * nph * max(args.steps, 1))

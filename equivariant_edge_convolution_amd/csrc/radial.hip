@@ -409,7 +409,7 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
   __shared__ SchedState st;
   sched_init<W>(sc, st);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int s = lane & 31, h = lane >> 5;
+  const int lane_s = lane & 31, lane_h = lane >> 5;
   const float* w1s = lds + Lds<C>::W1;
   const float* w2s = lds + Lds<C>::W2;
   const float* w3s = lds + Lds<C>::W3;
@@ -426,6 +426,10 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     }
     const int tile = (b - st.bstart[p]) * W + wave;
     if (tile >= st.ntile[p]) continue;
+    // re-derive the lane coordinates every tile: keeps the compiler from
+    // hoisting lane-dependent addresses out of the loop into spilled registers
+    int s = lane_s, h = lane_h;
+    asm volatile("" : "+v"(s), "+v"(h));
     const int64_t q = st.q0[p] + (int64_t)tile * 32 + s;
     const bool valid = q < st.q1[p];
     const int64_t qq = valid ? q : st.q0[p];
