@@ -34,9 +34,13 @@ sys.path.insert(0, ROOT)
 METRIC = "edges/s fwd+force bwd, fp32, 4096-atom diamond (E≈6.5e5); % of roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-# algorithmic flops per edge of the backward kernel (recomputation excluded)
-BWD_FLOP_PER_EDGE = 45056 + 2304 + 2048
-FWD_FLOP_PER_EDGE = 45056 + 2304
+# Algorithmic flops of the backward kernel (recomputation excluded).
+# direct: network input gradient 45,056 + Rbar 2,304 + Ybar 2,048 per edge.
+# folded: per edge Ybar = M s2 (2,048) + s2bar = M^T Y (2,048) + W2^T (8,192)
+#         + W1^T (4,096); per (receiver, sender species) unit M = Abar h W3^T
+#         (2 * 16 * 64 * 64 = 131,072).
+BWD_FLOP_PER_EDGE = {"direct": 45056 + 2304 + 2048, "folded": 2048 + 2048 + 8192 + 4096}
+BWD_FLOP_PER_UNIT = {"direct": 0, "folded": 2 * 16 * 64 * 64}
 WORKLOADS = {
     "D4096": "diamond 8x8x8 conventional cells, 4096 atoms, a=3.567 A, rc=6.0 A, 0.02 A noise, seed 0, C=64",
     "D512": "diamond 4x4x4 conventional cells, 512 atoms, rc=6.0 A, C=64",
@@ -122,6 +126,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="direct", choices=["direct", "folded"],
+                    help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
+                         "last radial layer moved past the edge sum (eec_energy_forces_folded)")
     ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy"],
                     help="energy_forces: the headline call; edge_message: the chunked streaming "
                          "forward (radial rows + message pass), for profiling its kernels; copy: a "
@@ -156,7 +163,7 @@ def main() -> int:
 
     if args.mode == "edge_message":
         return message_mode(args, B, torch, cfg, g, pos, species, model, dev)
-    ef = B.EnergyForces(g, model, dev, atom_energy=True)
+    ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=args.variant)
     nph = len(B.PHASES)
     ev = B.HipEvents(2 * nph * max(args.steps, 1))
     for _ in range(args.warmup):
@@ -176,7 +183,16 @@ def main() -> int:
     energy = float(ef.energy.cpu()[0])
 
     bwd_ms = phase_ms["backward"]
-    achieved = BWD_FLOP_PER_EDGE * E / (bwd_ms * 1e-3) / 1e12
+    # units with at least one edge: (receiver, sender species) pairs present in the graph
+    rp = g.row_ptr.cpu().numpy()
+    if cfg.model.n_species == 1:
+        n_units = int(np.count_nonzero(np.diff(rp)))
+    else:
+        col = g.col.cpu().numpy()
+        recv = np.repeat(np.arange(g.n_atoms), np.diff(rp))
+        n_units = len(np.unique(recv.astype(np.int64) * cfg.model.n_species + cfg.species[col]))
+    bwd_flop = BWD_FLOP_PER_EDGE[args.variant] * E + BWD_FLOP_PER_UNIT[args.variant] * n_units
+    achieved = bwd_flop / (bwd_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": E / (ms_per_step * 1e-3),
@@ -192,10 +208,12 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "n_atoms": cfg.n_atoms,
                    "n_edges": E, "channels": cfg.model.channels, "n_species": cfg.model.n_species},
-        "roofline": {"bound": "mfma", "kernel": "k_backward", "achieved": achieved,
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma",
+                     "kernel": "k_backward" if args.variant == "direct" else "k_fold_backward",
+                     "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                     "flop_per_edge": BWD_FLOP_PER_EDGE, "launch_ms": bwd_ms},
+                     "flop_per_launch": bwd_flop, "launch_ms": bwd_ms},
+        "variant": args.variant,
         "phases_ms": phase_ms,
         "neighbors_ms": nb_ms,
         "energy": energy,

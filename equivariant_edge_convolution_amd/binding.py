@@ -32,9 +32,11 @@ EEC_ERR_CAPACITY = 6
 SYMBOLS = (
     "eec_build_neighbors", "eec_neighbors_workspace_bytes", "eec_radial_basis",
     "eec_radial_project", "eec_project_workspace_bytes", "eec_edge_message",
-    "eec_energy_forces", "eec_energy_forces_timed", "eec_workspace_bytes", "eec_last_error",
+    "eec_energy_forces", "eec_energy_forces_folded", "eec_energy_forces_timed", "eec_workspace_bytes",
+    "eec_last_error",
 )
 PHASES = ("prepare", "forward", "readout", "backward", "scatter")
+VARIANTS = {"direct": 0, "folded": 1}
 
 
 class EECError(RuntimeError):
@@ -92,9 +94,11 @@ def lib() -> ctypes.CDLL:
     L.eec_edge_message.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, sz]
     L.eec_energy_forces.restype = ctypes.c_int
     L.eec_energy_forces.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz]
+    L.eec_energy_forces_folded.restype = ctypes.c_int
+    L.eec_energy_forces_folded.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz]
     L.eec_energy_forces_timed.restype = ctypes.c_int
     L.eec_energy_forces_timed.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz,
-                                          P(vp)]
+                                          i32, P(vp)]
     _lib = L
     return L
 
@@ -247,8 +251,10 @@ def edge_message(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, mo
 class EnergyForces:
     """Preallocated outputs + workspace for repeated eec_energy_forces calls."""
 
-    def __init__(self, graph: Graph, model: Model, device, atom_energy=True, virial=False):
+    def __init__(self, graph: Graph, model: Model, device, atom_energy=True, virial=False,
+                 variant: str = "direct"):
         n = graph.n_atoms
+        self.variant = VARIANTS[variant]
         self.graph, self.model = graph, model
         self.energy = torch.empty(1, dtype=torch.float32, device=device)
         self.atom_energy = torch.empty(n, dtype=torch.float32, device=device) if atom_energy else None
@@ -267,16 +273,18 @@ class EnergyForces:
                 _ptr(self.energy), _ptr(self.atom_energy), _ptr(self.forces), _ptr(self.virial),
                 _ptr(self.workspace), self.workspace.numel())
         if events is None:
-            _check(lib().eec_energy_forces(*args), "energy_forces")
+            fn = lib().eec_energy_forces if self.variant == 0 else lib().eec_energy_forces_folded
+            _check(fn(*args), "energy_forces")
         else:
             arr = (ctypes.c_void_p * len(events))(*events)
-            _check(lib().eec_energy_forces_timed(*args, arr), "energy_forces_timed")
+            _check(lib().eec_energy_forces_timed(*args, self.variant, arr), "energy_forces_timed")
         return self
 
 
 def energy_forces(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, model: Model,
-                  virial: bool = False):
-    ef = EnergyForces(graph, model, pos.device, atom_energy=True, virial=virial)
+                  virial: bool = False, variant: str = "direct"):
+    """eec_energy_forces (variant "direct") or eec_energy_forces_folded ("folded")."""
+    ef = EnergyForces(graph, model, pos.device, atom_energy=True, virial=virial, variant=variant)
     ef(pos, box, species)
     out = dict(energy=ef.energy, atom_energy=ef.atom_energy, forces=ef.forces)
     if virial:

@@ -235,7 +235,10 @@ eec_status eec_edge_message(void* stream, const eec_graph* g, const double* pos,
 static eec_status energy_forces_impl(void* stream, const eec_graph* g, const double* pos,
                                      const double* box, const int32_t* species, const eec_model* m,
                                      float* energy, float* atom_energy, float* forces, float* virial,
-                                     void* workspace, size_t workspace_bytes, void* const* events) {
+                                     void* workspace, size_t workspace_bytes, int32_t variant,
+                                     void* const* events) {
+  if (variant != EEC_VARIANT_DIRECT && variant != EEC_VARIANT_FOLDED)
+    return fail(EEC_ERR_SHAPE, "unknown variant");
   TRY(check_graph(g));
   TRY(check_model(m));
   TRY(check_box(box, m->cutoff));
@@ -266,7 +269,11 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   mark(2 * EEC_PHASE_PREPARE + 1);
   mark(2 * EEC_PHASE_FORWARD);
   int nparts = 1;
-  if (fused_forward_supported(p)) {
+  const bool folded = variant == EEC_VARIANT_FOLDED;
+  if (folded) {
+    launch_fold_forward(s, p, g, pos, b, m->cutoff, species, m, A, ws);  // S partial slabs
+    nparts = p.S;
+  } else if (fused_forward_supported(p)) {
     launch_forward(s, p, g, pos, b, m->cutoff, species, m, A, ws);  // S partial slabs
     nparts = p.S;
   } else {
@@ -282,7 +289,10 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   mark(2 * EEC_PHASE_READOUT + 1);
   float* gbuf = (float*)(ws + p.off_g);
   mark(2 * EEC_PHASE_BACKWARD);
-  launch_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);
+  if (folded)
+    launch_fold_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);
+  else
+    launch_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);
   mark(2 * EEC_PHASE_BACKWARD + 1);
   mark(2 * EEC_PHASE_SCATTER);
   launch_scatter(s, p, g, pos, b, gbuf, forces, (double*)(ws + p.off_vpart), virial);
@@ -294,15 +304,23 @@ eec_status eec_energy_forces(void* stream, const eec_graph* g, const double* pos
                              const int32_t* species, const eec_model* m, float* energy, float* atom_energy,
                              float* forces, float* virial, void* workspace, size_t workspace_bytes) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
-                            workspace_bytes, nullptr);
+                            workspace_bytes, EEC_VARIANT_DIRECT, nullptr);
+}
+
+eec_status eec_energy_forces_folded(void* stream, const eec_graph* g, const double* pos, const double* box,
+                                    const int32_t* species, const eec_model* m, float* energy,
+                                    float* atom_energy, float* forces, float* virial, void* workspace,
+                                    size_t workspace_bytes) {
+  return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
+                            workspace_bytes, EEC_VARIANT_FOLDED, nullptr);
 }
 
 eec_status eec_energy_forces_timed(void* stream, const eec_graph* g, const double* pos, const double* box,
                                    const int32_t* species, const eec_model* m, float* energy,
                                    float* atom_energy, float* forces, float* virial, void* workspace,
-                                   size_t workspace_bytes, void* const* events) {
+                                   size_t workspace_bytes, int32_t variant, void* const* events) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
-                            workspace_bytes, events);
+                            workspace_bytes, variant, events);
 }
 
 }  // extern "C"

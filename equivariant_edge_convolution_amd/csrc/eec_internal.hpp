@@ -44,7 +44,7 @@ struct ConvPlan {
   int64_t chunk;  // edges per streamed chunk
   size_t bytes;
   size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_seg, off_A, off_R, off_Y, off_g,
-      off_epart, off_vpart, off_ei;
+      off_epart, off_vpart, off_ei, off_w3t;
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
@@ -91,6 +91,15 @@ void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
 // Materialised basis / harmonics.
 void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box, double cutoff,
                   float* r, float* basis, float* Y);
+
+// Reassociated last layer (the fold): forward per unit into the S partial A
+// slabs; backward (also writes the transposed last-layer weights it reads).
+void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                         Box box, double cutoff, const int32_t* species, const eec_model* m,
+                         float* A_out, const char* ws);
+void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                          Box box, double cutoff, const int32_t* species, const eec_model* m,
+                          const float* Abar, float* gout, char* ws);
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

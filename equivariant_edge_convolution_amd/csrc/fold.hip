@@ -1,0 +1,395 @@
+// The energy/force call with the linear last radial layer moved past the
+// edge sum (exact algebra, the fold of "deepmd-kit PR #6108", What: a frozen
+// linear map applied after a linear reduction may be applied once, after it).
+//
+// Forward, per (pair p = (Z_i, s), receiver i) unit:
+//   T_{k,lm} = sum_{e in row i, Z_j = s} s2_{e,k} Y_{e,lm}          (matrix cores, K = edges)
+//   A^{(s)}_{i,lm,c} = h_{s,c} sum_k T_{k,lm} W3_p[k, l(lm) C + c]   (per receiver)
+// instead of R_e = s2_e W3 for every edge: 45,056 -> 12,288 + 2,048 flop per
+// edge plus 131,072 flop per unit.
+// Backward, per unit, with Abar = dE/dA:
+//   M_{lm,k} = sum_c Abar_{i,lm,c} h_{s,c} W3_p[k, l(lm) C + c]      (per receiver)
+//   Ybar_{e,lm} = sum_k s2_{e,k} M_{lm,k},   s2bar_{e,k} = sum_lm M_{lm,k} Y_{e,lm}
+// which replace recomputing R (32,768 flop/edge) and s2bar = Rbar W3^T
+// (32,768 flop/edge) by 4,096 flop/edge.  The rest of the backward (SiLU
+// derivatives, W2^T, W1^T, the radial and angular chain rule) is the direct
+// path's.
+#include "chain.hpp"
+
+namespace eec {
+namespace {
+using namespace chain;
+
+// ------------------------------------------------------------------ forward
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
+               const float* __restrict__ W3, const float* __restrict__ emb, float* __restrict__ A_out) {
+  constexpr int NC = 4 * C, CPL = C / 64;
+  __shared__ float w12[W12_FLOATS];
+  __shared__ float ysm[W][32][NLM + 1];  // harmonics of the tile's edges (zero rows for padding)
+  __shared__ float tsm[W][HID][NLM];     // T of the unit, staged for the last layer
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane_s = lane & 31, lane_h = lane >> 5;
+  const float* w1s = w12;
+  const float* w2s = w12 + NB * LDH;
+  const int N = un.n_atoms, S = un.S, P = S * S;
+  const int nbp = (N + W - 1) / W;
+  int loaded = -1;
+  for (int b = blockIdx.x; b < P * nbp; b += gridDim.x) {
+    const int p = b / nbp;
+    if (p != loaded) {
+      __syncthreads();
+      stage_w12(w12, W1, W2, p);
+      __syncthreads();
+      loaded = p;
+    }
+    const int i = (b - p * nbp) * W + wave;
+    int qa, qb;
+    if (i >= N || !unit_range(un, p, i, qa, qb)) continue;
+    int s = lane_s, h = lane_h;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int zs = p % S;
+    f32x16 T[2];
+    T[0] = zero16();
+    T[1] = zero16();
+    for (int q0 = qa; q0 < qb; q0 += 32) {
+      const int q = q0 + s;
+      const bool valid = q < qb;
+      const int qq = valid ? q : qa;
+      const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
+      const Geo g = edge_geo(in, e);
+      f32x16 z[2], a[2];
+      {
+        float bas[16];
+        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+        layer1(w1s, bas, s, h, z);
+      }
+      silu_tiles(z, a);  // s1, edges on N
+      // z2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s
+      {
+        const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
+        z[0] = zero16();
+        z[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const float av = a[ks >> 4][ks & 15];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) z[m] = mfma32(av, w[hid_k0(ks) * LDH + 32 * m], z[m]);
+        }
+      }
+      silu_tiles(z, a);  // s2, edges on M
+      {
+        float Y[16];
+        sph16(g.ux, g.uy, g.uz, Y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ysm[wave][s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
+      }
+      wave_sync_lds();
+      // T[hidden][lm] += sum over this tile's edges (K = edges, pairs (fperm(ks), fperm(ks)+4))
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const float yv = s < NLM ? ysm[wave][fperm(ks) + 4 * h][s] : 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) T[m] = mfma32(a[m][ks], yv, T[m]);
+      }
+      wave_sync_lds();
+    }
+    // T register r of tile m, lane (s, h): hidden 32 m + fperm(r) + 4h, harmonic s (< 16)
+    if (s < NLM) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tsm[wave][32 * m + fperm(r) + 4 * h][s] = T[m][r];
+    }
+    wave_sync_lds();
+    // A[lm][c] = h_c sum_k T[k][lm] W3[k][l(lm) C + c]; lane = channel(s)
+    const float* w3 = W3 + (size_t)p * HID * NC;
+    float acc[CPL][NLM];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < HID; ++k) {
+      float t[NLM];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 x = *reinterpret_cast<const float4*>(&tsm[wave][k][4 * v]);
+        t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
+      }
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const float* wr = w3 + (size_t)k * NC + lane + 64 * q;
+        const float w0 = wr[0], wl1 = wr[C], wl2 = wr[2 * C], wl3 = wr[3 * C];
+        acc[q][0] += t[0] * w0;
+#pragma unroll
+        for (int lm = 1; lm < 4; ++lm) acc[q][lm] += t[lm] * wl1;
+#pragma unroll
+        for (int lm = 4; lm < 9; ++lm) acc[q][lm] += t[lm] * wl2;
+#pragma unroll
+        for (int lm = 9; lm < 16; ++lm) acc[q][lm] += t[lm] * wl3;
+      }
+    }
+    float* ao = A_out + ((size_t)zs * N + i) * NLM * C;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c = lane + 64 * q;
+      const float hc = emb[(size_t)zs * C + c];
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) ao[k * C + c] = hc * acc[q][k];
+    }
+    wave_sync_lds();
+  }
+}
+
+// ------------------------------------------------------------------ backward
+constexpr int AHS = NLM + 4;  // row stride of the staged Abar h rows (16-byte aligned)
+
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
+                const float* __restrict__ W3T, const float* __restrict__ emb,
+                const float* __restrict__ Abar, float* __restrict__ gout) {
+  constexpr int NC = 4 * C, CPL = C / 64;
+  __shared__ float w12[W12_FLOATS];
+  __shared__ float ahsm[W][C][AHS];         // Abar_{lm,c} h_c, row c
+  __shared__ float msm[W][NLM][HID + 1];    // M_{lm,k}
+  __shared__ float ybsm[W][32][NLM + 1];    // Ybar of the tile, row = edge slot
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane_s = lane & 31, lane_h = lane >> 5;
+  const float* w1s = w12;
+  const float* w2s = w12 + NB * LDH;
+  const int N = un.n_atoms, S = un.S, P = S * S;
+  const int nbp = (N + W - 1) / W;
+  int loaded = -1;
+  for (int b = blockIdx.x; b < P * nbp; b += gridDim.x) {
+    const int p = b / nbp;
+    if (p != loaded) {
+      __syncthreads();
+      stage_w12(w12, W1, W2, p);
+      __syncthreads();
+      loaded = p;
+    }
+    const int i = (b - p * nbp) * W + wave;
+    int qa, qb;
+    if (i >= N || !unit_range(un, p, i, qa, qb) || qb <= qa) continue;
+    int s = lane_s, h = lane_h;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int zs = p % S;
+    // stage Abar_i h_s (lane = channel)
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c = lane + 64 * q;
+      const float hc = emb[(size_t)zs * C + c];
+      const float* ar = Abar + (size_t)i * NLM * C + c;
+#pragma unroll
+      for (int lm = 0; lm < NLM; ++lm) ahsm[wave][c][lm] = ar[lm * C] * hc;
+    }
+    wave_sync_lds();
+    // M[lm][k] = sum_c Abar h [lm][c] W3[k][l(lm) C + c]; lane = hidden k
+    {
+      const float* wt = W3T + (size_t)p * NC * HID + lane;  // W3T[p][j][k] = W3[p][k][j]
+      float macc[NLM];
+#pragma unroll
+      for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < C; ++c) {
+        float av[NLM];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 x = *reinterpret_cast<const float4*>(&ahsm[wave][c][4 * v]);
+          av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
+        }
+        const float w0 = wt[(size_t)c * HID], wl1 = wt[(size_t)(C + c) * HID];
+        const float wl2 = wt[(size_t)(2 * C + c) * HID], wl3 = wt[(size_t)(3 * C + c) * HID];
+        macc[0] += av[0] * w0;
+#pragma unroll
+        for (int lm = 1; lm < 4; ++lm) macc[lm] += av[lm] * wl1;
+#pragma unroll
+        for (int lm = 4; lm < 9; ++lm) macc[lm] += av[lm] * wl2;
+#pragma unroll
+        for (int lm = 9; lm < 16; ++lm) macc[lm] += av[lm] * wl3;
+      }
+#pragma unroll
+      for (int lm = 0; lm < NLM; ++lm) msm[wave][lm][lane] = macc[lm];
+    }
+    wave_sync_lds();
+
+    for (int q0 = qa; q0 < qb; q0 += 32) {
+      const int q = q0 + s;
+      const bool valid = q < qb;
+      const int qq = valid ? q : qa;
+      const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
+      const Geo g = edge_geo(in, e);
+      f32x16 z1[2], z2[2], s2[2];
+      {
+        float bas[16];
+        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+        layer1(w1s, bas, s, h, z1);
+      }
+      {
+        f32x16 s1[2];
+        silu_tiles(z1, s1);
+        layer2(w2s, s1, s, h, z2);
+      }
+      silu_tiles(z2, s2);  // edges on N
+      __builtin_amdgcn_sched_barrier(0);
+      // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k]  (edges on M; lane column = lm)
+      f32x16 yb = zero16();
+      {
+        const float* mr = &msm[wave][s < NLM ? s : 0][4 * h];
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const float bv = s < NLM ? mr[hid_k0(ks)] : 0.f;
+          yb = mfma32(s2[ks >> 4][ks & 15], bv, yb);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // s2bar[k][edge] = sum_lm M[lm][k] Y[edge][lm]  (edges on N; K pairs (2ks, 2ks + 1))
+      f32x16 sb[2];
+      sb[0] = zero16();
+      sb[1] = zero16();
+      {
+        float Y[16];
+        sph16(g.ux, g.uy, g.uz, Y);
+        const float* mc = &msm[wave][h][s];  // M[2 ks + h][32 m + s]
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const float bv = h ? Y[2 * ks + 1] : Y[2 * ks];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) sb[m] = mfma32(mc[2 * ks * (HID + 1) + 32 * m], bv, sb[m]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Ybar to the lanes that own the edges, contracted with the harmonic gradients
+      if (s < NLM) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ybsm[wave][fperm(r) + 4 * h][s] = yb[r];
+      }
+      wave_sync_lds();
+      float G[3];
+      {
+        float ybe[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ybe[k] = ybsm[wave][s][k];
+        sph16_grad_dot(g.ux, g.uy, g.uz, ybe, G);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[m][r] *= silu_d(z2[m][r]);  // z2bar
+      f32x16 s1b[2];
+      s1b[0] = zero16();
+      s1b[1] = zero16();
+      const float* w2c = w2s + s * LDH + 4 * h;  // W2[32 m + s][hid_k0(ks) + 4 h]
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) {
+        const float bv = sb[ks >> 4][ks & 15];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s1b[m] = mfma32(w2c[32 * m * LDH + hid_k0(ks)], bv, s1b[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s1b[m][r] *= silu_d(z1[m][r]);  // z1bar
+      f32x16 bb = zero16();
+      const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) bb = mfma32(w1c[hid_k0(ks)], s1b[ks >> 4][ks & 15], bb);
+      __builtin_amdgcn_sched_barrier(0);
+      float rbar = 0.f;
+      {
+        float bas[16], dbas[16];
+        basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
+      }
+      rbar += __shfl_xor(rbar, 32);
+      const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
+      if (valid && h == 0) {
+        gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
+        gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
+        gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+      }
+      wave_sync_lds();
+    }
+  }
+}
+
+// W3T[p][j][k] = W3[p][k][j]: the backward reads W3 down its columns.
+__global__ void k_transpose_w3(int P, int NC, const float* __restrict__ W3, float* __restrict__ W3T) {
+  const int64_t n = (int64_t)P * HID * NC;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = t / ((int64_t)HID * NC), rem = t % ((int64_t)HID * NC);
+    const int k = (int)(rem / NC), j = (int)(rem % NC);
+    W3T[(p * NC + j) * HID + k] = W3[t];
+  }
+}
+
+constexpr int WAVES = 8;
+
+EdgeIn make_in_f(const ConvPlan& p, const eec_graph* g, const double* pos, Box box, double cutoff,
+                 const int32_t* species, const char* ws) {
+  EdgeIn in;
+  in.pos = pos;
+  in.Lx = box.L[0];
+  in.Ly = box.L[1];
+  in.Lz = box.L[2];
+  in.rc = cutoff;
+  in.recv = (const int32_t*)(ws + p.off_recv);
+  in.col = g->col;
+  in.shift = g->shift;
+  in.species = species;
+  in.n_atoms = g->n_atoms;
+  in.n_edges = g->n_edges;
+  return in;
+}
+
+Units make_units(const ConvPlan& p, const eec_graph* g, const int32_t* species, const char* ws) {
+  Units un;
+  un.row_ptr = g->row_ptr;
+  un.species = species;
+  un.perm = p.S > 1 ? (const int32_t*)(ws + p.off_perm) : nullptr;
+  un.seg = p.S > 1 ? (const int32_t*)(ws + p.off_seg) : nullptr;
+  un.n_atoms = p.N;
+  un.S = p.S;
+  return un;
+}
+
+int unit_grid(const ConvPlan& p) {
+  const int64_t batches = (int64_t)p.P * ((p.N + WAVES - 1) / WAVES);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(batches, 256));
+}
+
+}  // namespace
+
+void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                         Box box, double cutoff, const int32_t* species, const eec_model* m,
+                         float* A_out, const char* ws) {
+  if (p.N == 0) return;
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species, ws);
+  const Units un = make_units(p, g, species, ws);
+  if (p.C == 64)
+    k_fold_forward<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, m->emb, A_out);
+  else
+    k_fold_forward<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, m->emb, A_out);
+}
+
+void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
+                          Box box, double cutoff, const int32_t* species, const eec_model* m,
+                          const float* Abar, float* gout, char* ws) {
+  if (p.N == 0 || p.E == 0) return;
+  float* W3T = (float*)(ws + p.off_w3t);
+  const int64_t n = (int64_t)p.P * HID * p.NC;
+  k_transpose_w3<<<(int)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, s>>>(p.P, p.NC, m->W3, W3T);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species, ws);
+  const Units un = make_units(p, g, species, ws);
+  if (p.C == 64)
+    k_fold_backward<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, W3T, m->emb, Abar, gout);
+  else
+    k_fold_backward<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, W3T, m->emb, Abar, gout);
+}
+
+}  // namespace eec

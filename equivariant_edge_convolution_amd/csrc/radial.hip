@@ -23,168 +23,11 @@
 // pair's weights in LDS and walks "batches" of W tiles of that pair, grid-stride.
 #include <algorithm>
 
-#include "eec_device.hpp"
-#include "eec_internal.hpp"
+#include "chain.hpp"
 
 namespace eec {
 namespace {
-
-constexpr int MAXP = 16;
-
-// Weights in LDS, row-major with one padding column: a wave reading along a row
-// (lanes over columns) or down a column (lanes over rows) touches 32 distinct
-// banks either way, and every address is a per-lane base plus an immediate.
-constexpr int LDH = HID + 1;  // row stride of W1 [32][64] and W2 [64][64]
-template <int C>
-struct Lds {
-  static constexpr int NC = 4 * C;
-  static constexpr int LD3 = NC + 1;            // row stride of W3 [64][NC]
-  static constexpr int W1 = 0;
-  static constexpr int W2 = W1 + NB * LDH;
-  static constexpr int W3 = W2 + HID * LDH;
-  static constexpr int FLOATS = W3 + HID * LD3;  // 90752 B (C=64), 156288 B (C=128)
-};
-
-struct EdgeIn {
-  const double* pos;
-  double Lx, Ly, Lz, rc;
-  const int32_t* recv;
-  const int32_t* col;
-  const int8_t* shift;
-  const int32_t* species;
-  int32_t n_atoms;
-  int64_t n_edges;
-};
-
-struct Sched {
-  const int32_t* perm;        // pair-grouped order -> CSR edge; NULL = identity
-  const int64_t* pair_start;  // [P+1] group offsets in that order; NULL = one group [0, E)
-  int P;
-  int64_t e0, e1;             // CSR edge range to process
-};
-
-struct SchedState {
-  int64_t q0[MAXP], q1[MAXP];
-  int bstart[MAXP + 1];
-  int ntile[MAXP];
-};
-
-// Lower bound of CSR index `e` among positions [lo, hi) of a pair group.
-__device__ int64_t group_lower_bound(const int32_t* perm, int64_t lo, int64_t hi, int64_t e) {
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if ((int64_t)perm[mid] < e) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-template <int W>
-__device__ void sched_init(const Sched& sc, SchedState& st) {
-  const int t = threadIdx.x;
-  if (t < sc.P) {
-    int64_t q0, q1;
-    if (sc.perm == nullptr) {
-      q0 = sc.e0;
-      q1 = sc.e1;
-    } else {
-      const int64_t g0 = sc.pair_start[t], g1 = sc.pair_start[t + 1];
-      q0 = group_lower_bound(sc.perm, g0, g1, sc.e0);
-      q1 = group_lower_bound(sc.perm, q0, g1, sc.e1);
-    }
-    st.q0[t] = q0;
-    st.q1[t] = q1;
-    st.ntile[t] = (int)((q1 - q0 + 31) / 32);
-  }
-  __syncthreads();
-  if (t == 0) {
-    int acc = 0;
-    for (int p = 0; p < sc.P; ++p) {
-      st.bstart[p] = acc;
-      acc += (st.ntile[p] + W - 1) / W;
-    }
-    st.bstart[sc.P] = acc;
-  }
-  __syncthreads();
-}
-
-template <int C>
-__device__ void stage_weights(float* lds, const float* __restrict__ W1, const float* __restrict__ W2,
-                              const float* __restrict__ W3, int p) {
-  constexpr int NC = Lds<C>::NC;
-  const float* w1 = W1 + (size_t)p * NB * HID;
-  const float* w2 = W2 + (size_t)p * HID * HID;
-  const float* w3 = W3 + (size_t)p * HID * NC;
-  for (int k = threadIdx.x; k < NB * HID; k += blockDim.x)
-    lds[Lds<C>::W1 + (k / HID) * LDH + k % HID] = w1[k];
-  for (int k = threadIdx.x; k < HID * HID; k += blockDim.x)
-    lds[Lds<C>::W2 + (k / HID) * LDH + k % HID] = w2[k];
-  for (int k = threadIdx.x; k < HID * NC; k += blockDim.x)
-    lds[Lds<C>::W3 + (k / NC) * Lds<C>::LD3 + k % NC] = w3[k];
-}
-
-// Input hidden feature of K-step ks (0..31) carried by a lane of half h when the
-// 64 hidden features sit in two edges-on-N accumulator tiles: hid_k0(ks) + 4 h.
-__device__ __forceinline__ constexpr int hid_k0(int ks) { return 32 * (ks >> 4) + fperm(ks & 15); }
-
-// z1 = b W1 (edges on N): two 32-feature tiles.
-__device__ __forceinline__ void layer1(const float* __restrict__ w1s, const float b[16], int s, int h,
-                                       f32x16 z[2]) {
-  const float* w = w1s + 16 * h * LDH + s;  // W1[16 h + ks][32 m + s]
-  z[0] = zero16();
-  z[1] = zero16();
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) z[m] = mfma32(w[ks * LDH + 32 * m], b[ks], z[m]);
-}
-
-// z2 = s1 W2 (edges on N).
-__device__ __forceinline__ void layer2(const float* __restrict__ w2s, const f32x16 s1[2], int s, int h,
-                                       f32x16 z[2]) {
-  const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
-  z[0] = zero16();
-  z[1] = zero16();
-#pragma unroll
-  for (int ks = 0; ks < 32; ++ks) {
-    const float bv = s1[ks >> 4][ks & 15];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) z[m] = mfma32(w[hid_k0(ks) * LDH + 32 * m], bv, z[m]);
-  }
-}
-
-__device__ __forceinline__ void silu_tiles(const f32x16 z[2], f32x16 s[2]) {
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[m][r] = silu(z[m][r]);
-}
-
-// Geometry of the edge a lane works on (binary64, as the neighbour list).
-struct Geo {
-  double r;
-  float ux, uy, uz, inv_r;
-  int i, j;
-};
-
-__device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) {
-  Geo g;
-  int i = in.recv[e], j = in.col[e];
-  i = min(max(i, 0), in.n_atoms - 1);
-  j = min(max(j, 0), in.n_atoms - 1);
-  double d[3];
-  edge_vector(in.pos, i, j, in.shift + 3 * e, in.Lx, in.Ly, in.Lz, d);
-  const double r2 = norm2_nofma(d);
-  const double r = sqrt(r2);
-  const double ir = 1.0 / r;
-  g.r = r;
-  g.inv_r = (float)ir;
-  g.ux = (float)(d[0] * ir);
-  g.uy = (float)(d[1] * ir);
-  g.uz = (float)(d[2] * ir);
-  g.i = i;
-  g.j = j;
-  return g;
-}
+using namespace chain;
 
 // ------------------------------------------------------------------ forward
 // With `emb` non-NULL the rows written are rho = R h_{Z_j} (the sender embedding
@@ -281,14 +124,7 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
 // harmonics go through a per-wave LDS slot (rows of padding edges are zero).
 // No radial row ever leaves the chip.  Output: the unit's partial A (sender
 // species s) at A_out + (s * N + i) * 16 * C.
-struct Units {
-  const int32_t* row_ptr;
-  const int32_t* species;
-  const int32_t* perm;   // pair-grouped order -> CSR edge (S > 1); NULL when S == 1
-  const int32_t* seg;    // [S][N][2] position range of unit (i, s) in that order (S > 1)
-  int32_t n_atoms;
-  int S;
-};
+
 
 template <int W>
 __global__ void __launch_bounds__(64 * W)

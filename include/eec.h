@@ -203,24 +203,46 @@ EEC_API eec_status eec_energy_forces(void *stream, const eec_graph *g, const dou
                              size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
- * eec_energy_forces_timed -- eec_energy_forces, with hipEvent_t handles
+ * eec_energy_forces_folded -- the same outputs as eec_energy_forces (equal up
+ * to float32 rounding), with the linear last radial layer moved past the edge
+ * sum: the fold of a frozen linear map applied after a linear reduction
+ * ("deepmd-kit PR #6108", What; exact in real arithmetic, "Accuracy").
+ *   forward:  T_{i,s}[k][lm] = sum_{e in row i, Z_j = s} silu(z2_e)[k] Y_e[lm],
+ *             A_i[lm][c] = sum_s h_{s,c} sum_k T_{i,s}[k][lm] W3_{(Z_i,s)}[k][l C + c];
+ *   backward: M_{i,s}[lm][k] = sum_c (dE/dA_i)[lm][c] h_{s,c} W3_{(Z_i,s)}[k][l C + c],
+ *             dE/dY_e = M s2_e,  dE/ds2_e = M^T Y_e.
+ * The per-edge radial weights R are never formed.  Arguments as
+ * eec_energy_forces; same workspace size. */
+EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, const double *pos,
+                                    const double *box /*[host][3]*/, const int32_t *species,
+                                    const eec_model *m, float *energy, float *atom_energy,
+                                    float *forces, float *virial, void *workspace,
+                                    size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
+ * eec_energy_forces_timed -- eec_energy_forces (variant EEC_VARIANT_DIRECT) or
+ * eec_energy_forces_folded (EEC_VARIANT_FOLDED), with hipEvent_t handles
  * (created by the caller, e.g. with hipEventCreate) recorded on `stream` around
  * each phase: events[2k] before and events[2k+1] after phase k, for
  *   k = EEC_PHASE_PREPARE   receiver index and pair grouping,
- *       EEC_PHASE_FORWARD   radial network + message over all edge chunks,
+ *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
+ *                           radial-row chunks and message passes),
  *       EEC_PHASE_READOUT   per-atom energies, dE/dA, total energy,
- *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch),
+ *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch; the
+ *                           folded variant also transposes W3 first),
  *       EEC_PHASE_SCATTER   forces (and virial).
- * `events` holds 2 * EEC_N_PHASES handles; NULL behaves as eec_energy_forces.
- * Same results, bit for bit, as eec_energy_forces. */
+ * `events` holds 2 * EEC_N_PHASES handles; NULL records nothing.  Results are
+ * bit for bit those of the untimed call. */
 enum { EEC_PHASE_PREPARE = 0, EEC_PHASE_FORWARD = 1, EEC_PHASE_READOUT = 2,
        EEC_PHASE_BACKWARD = 3, EEC_PHASE_SCATTER = 4, EEC_N_PHASES = 5 };
+enum { EEC_VARIANT_DIRECT = 0, EEC_VARIANT_FOLDED = 1 };
 
 EEC_API eec_status eec_energy_forces_timed(void *stream, const eec_graph *g, const double *pos,
                                    const double *box /*[host][3]*/, const int32_t *species,
                                    const eec_model *m, float *energy, float *atom_energy,
                                    float *forces, float *virial, void *workspace,
-                                   size_t workspace_bytes, void *const *events);
+                                   size_t workspace_bytes, int32_t variant,
+                                   void *const *events);
 
 EEC_API size_t eec_workspace_bytes(int32_t n_atoms, int64_t n_edges, const eec_model *m);
 

@@ -20,18 +20,22 @@ pytestmark = pytest.mark.gpu
 SMALL = ["D64", "RS2", "RS3", "PV2", "PV3", "D64c128", "D512", "D512c128"]
 
 
-def _run(name, virial=False):
+VARIANTS = ["direct", "folded"]
+
+
+def _run(name, virial=False, variant="direct"):
     cfg = I.make_config(name)
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
-    out = B.energy_forces(g, pos, cfg.box, species, model, virial=virial)
+    out = B.energy_forces(g, pos, cfg.box, species, model, virial=virial, variant=variant)
     return cfg, pos, species, model, g, {k: np_(v) for k, v in out.items()}
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("name", SMALL)
-def test_energy_forces_elementwise(name):
-    say(f"[energy_forces] {name}")
-    cfg, *_, got = _run(name, virial=True)
+def test_energy_forces_elementwise(name, variant):
+    say(f"[energy_forces] {name} {variant}")
+    cfg, *_, got = _run(name, virial=True, variant=variant)
     ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
     for k in ("energy", "atom_energy", "forces", "virial"):
         assert np.all(np.isfinite(got[k])), k
@@ -56,12 +60,13 @@ def test_edge_message(name):
     assert np.abs(A - A0).max() <= 2e-5 * np.abs(A0).max()
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("name,n_e,n_f", [("D4096", 256, 3), ("RS", 256, 6), ("PV", 256, 4), ("D32k", 96, 2)])
-def test_full_size_sampled(name, n_e, n_f):
+def test_full_size_sampled(name, n_e, n_f, variant):
     """Full-size cells in the benchmark's launch configuration; exact per-atom
     energies and forces of sampled atoms from the oracle."""
-    say(f"[full-size] {name}")
-    cfg, pos, species, model, g, got = _run(name)
+    say(f"[full-size] {name} {variant}")
+    cfg, pos, species, model, g, got = _run(name, variant=variant)
     for k in ("energy", "atom_energy", "forces"):
         assert np.all(np.isfinite(got[k])), k
     csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
@@ -83,19 +88,39 @@ def test_full_size_sampled(name, n_e, n_f):
 def test_full_energy_headline_cell():
     """Total energy of the 4096-atom diamond against the full oracle forward."""
     say("[full-size] D4096 total energy")
-    cfg, *_, got = _run("D4096")
-    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
-    E0 = M.forward_edges(N.edge_vectors(cfg.pos, cfg.box, csr), csr, cfg.species, cfg.model)["E"]
-    assert abs(float(got["energy"][0]) - E0) <= 1e-5 * abs(E0)
+    csr = None
+    for variant in VARIANTS:
+        cfg, *_, got = _run("D4096", variant=variant)
+        if csr is None:
+            csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+            E0 = M.forward_edges(N.edge_vectors(cfg.pos, cfg.box, csr), csr, cfg.species, cfg.model)["E"]
+        assert abs(float(got["energy"][0]) - E0) <= 1e-5 * abs(E0), variant
 
 
-def test_bitwise_repeatable():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bitwise_repeatable(variant):
     cfg = I.make_config("PV3")
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
-    ef = B.EnergyForces(g, model, pos.device, virial=True)
+    ef = B.EnergyForces(g, model, pos.device, virial=True, variant=variant)
     ef(pos, cfg.box, species)
     E, F, W = ef.energy.clone(), ef.forces.clone(), ef.virial.clone()
     for _ in range(20):
         ef(pos, cfg.box, species)
         assert torch.equal(ef.energy, E) and torch.equal(ef.forces, F) and torch.equal(ef.virial, W)
+
+
+def test_timed_entry_point_matches_untimed():
+    cfg = I.make_config("RS3")
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    for variant in VARIANTS:
+        ef = B.EnergyForces(g, model, pos.device, variant=variant)
+        ef(pos, cfg.box, species)
+        E, F = ef.energy.clone(), ef.forces.clone()
+        ev = B.HipEvents(2 * len(B.PHASES))
+        ef(pos, cfg.box, species, events=ev.handles)
+        torch.cuda.synchronize()
+        assert torch.equal(ef.energy, E) and torch.equal(ef.forces, F)
+        assert all(ev.elapsed_ms(2 * k, 2 * k + 1) >= 0 for k in range(len(B.PHASES)))
+        ev.close()
