@@ -6,15 +6,21 @@ Default workload: the 4096-atom carbon diamond (8 x 8 x 8 conventional cells,
 a = 3.567 A, 0.02 A seeded noise, cutoff 6.0 A, E = 647,168 directed edges),
 one species, 64 channels.  Inputs are synthetic and seeded (eec_inputs); the
 neighbour list is built once before timing (it is timed separately and
-reported as context).  Each timed step is one full eec_energy_forces call:
-radial network + streamed message + readout + streaming backward + force
-scatter, with every input already resident in device memory.
+reported as context).  Each timed step is one full energy/force call with
+every input already resident in device memory: radial network + message +
+readout + streaming backward + force scatter.
+
+The headline variant (--variant, default "folded") is eec_energy_forces_folded:
+the linear last radial layer applied once per receiver instead of once per
+edge (same outputs up to float32 rounding).  The other variant ("direct",
+eec_energy_forces: the radial weights R of every edge on matrix cores) is
+timed in the same run and reported under "variants".
 
 Also reported:
   roofline      the dominant kernel (the streaming backward), its launch
                 duration measured with hipEvents recorded by the library on
-                the stream it launches on; algorithmic flops per edge
-                (network input gradient 45,056 + Rbar 2,304 + Ybar 2,048)
+                the stream it launches on; its algorithmic flops (see
+                BWD_FLOP_PER_EDGE / BWD_FLOP_PER_UNIT; recomputation excluded)
                 over that duration, against the FP32 matrix peak;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
                 (all receivers of the cell: their forward and force backward),
@@ -126,7 +132,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", default="direct", choices=["direct", "folded"],
+    ap.add_argument("--variant", default="folded", choices=["direct", "folded"],
                     help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
                          "last radial layer moved past the edge sum (eec_energy_forces_folded)")
     ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy"],
@@ -163,24 +169,28 @@ def main() -> int:
 
     if args.mode == "edge_message":
         return message_mode(args, B, torch, cfg, g, pos, species, model, dev)
-    ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=args.variant)
-    nph = len(B.PHASES)
-    ev = B.HipEvents(2 * nph * max(args.steps, 1))
-    for _ in range(args.warmup):
-        ef(pos, cfg.box, species)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ef(pos, cfg.box, species, events=ev.handles[2 * nph * k: 2 * nph * (k + 1)])
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt * 1e3 / args.steps
-    phase_ms = {}
-    for p, name in enumerate(B.PHASES):
-        phase_ms[name] = float(np.mean([ev.elapsed_ms(2 * nph * k + 2 * p, 2 * nph * k + 2 * p + 1)
-                                        for k in range(args.steps)]))
-    ev.close()
-    energy = float(ef.energy.cpu()[0])
+    def timed(variant, steps, warmup):
+        ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=variant)
+        nph = len(B.PHASES)
+        ev = B.HipEvents(2 * nph * max(steps, 1))
+        for _ in range(warmup):
+            ef(pos, cfg.box, species)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            ef(pos, cfg.box, species, events=ev.handles[2 * nph * k: 2 * nph * (k + 1)])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        phase_ms = {}
+        for p, name in enumerate(B.PHASES):
+            phase_ms[name] = float(np.mean([ev.elapsed_ms(2 * nph * k + 2 * p, 2 * nph * k + 2 * p + 1)
+                                            for k in range(steps)]))
+        ev.close()
+        return dt * 1e3 / steps, phase_ms, float(ef.energy.cpu()[0])
+
+    ms_per_step, phase_ms, energy = timed(args.variant, args.steps, args.warmup)
+    other = "direct" if args.variant == "folded" else "folded"
+    o_ms, o_phase, o_energy = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
     bwd_ms = phase_ms["backward"]
     # units with at least one edge: (receiver, sender species) pairs present in the graph
@@ -191,8 +201,11 @@ def main() -> int:
         col = g.col.cpu().numpy()
         recv = np.repeat(np.arange(g.n_atoms), np.diff(rp))
         n_units = len(np.unique(recv.astype(np.int64) * cfg.model.n_species + cfg.species[col]))
-    bwd_flop = BWD_FLOP_PER_EDGE[args.variant] * E + BWD_FLOP_PER_UNIT[args.variant] * n_units
-    achieved = bwd_flop / (bwd_ms * 1e-3) / 1e12
+
+    def bwd_flop(variant):
+        return BWD_FLOP_PER_EDGE[variant] * E + BWD_FLOP_PER_UNIT[variant] * n_units
+
+    achieved = bwd_flop(args.variant) / (bwd_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": E / (ms_per_step * 1e-3),
@@ -212,8 +225,12 @@ def main() -> int:
                      "kernel": "k_backward" if args.variant == "direct" else "k_fold_backward",
                      "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                     "flop_per_launch": bwd_flop, "launch_ms": bwd_ms},
+                     "flop_per_launch": bwd_flop(args.variant), "launch_ms": bwd_ms},
         "variant": args.variant,
+        "variants": {other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase,
+                             "energy": o_energy,
+                             "backward_frac": bwd_flop(other) / (o_phase["backward"] * 1e-3) / 1e12
+                             / PEAK_FP32_MFMA_TFLOPS}},
         "phases_ms": phase_ms,
         "neighbors_ms": nb_ms,
         "energy": energy,

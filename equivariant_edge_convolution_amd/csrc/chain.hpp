@@ -134,6 +134,18 @@ __device__ __forceinline__ void layer2(const float* __restrict__ w2s, const f32x
   }
 }
 
+// s = silu(z) and d = silu'(z) from one sigmoid evaluation.
+__device__ __forceinline__ void silu_and_deriv(const f32x16 z[2], f32x16 s[2], f32x16 d[2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float zz = z[m][r], sg = sigmoid(zz);
+      s[m][r] = zz * sg;
+      d[m][r] = sg * (1.f + zz * (1.f - sg));
+    }
+}
+
 __device__ __forceinline__ void silu_tiles(const f32x16 z[2], f32x16 s[2]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)

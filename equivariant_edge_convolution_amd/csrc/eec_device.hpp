@@ -84,15 +84,40 @@ __device__ __forceinline__ double envelope_d(double x) {
   return -168.0 * x5 * om * om;
 }
 
-// Basis functions n = n0 .. n0 + 15 (1-based n0) of b_n = sin(n pi r / rc) / r * env(r / rc)
-// for one lane half, by the angle-addition recurrence in binary64 from one sincos
-// pair at n0 and one at the step angle; optionally db_n / dr.
+// Start of the basis recurrence of a lane half h: the sine and cosine of
+// n0 theta, n0 = 16 h + 1, theta = pi r / rc, and of the step theta.  One
+// binary64 sincos; the n0 = 17 start comes from four angle doublings
+// (16 theta) and one rotation by theta, which costs a few ulps of binary64.
+struct BasisStart {
+  double s, c;    // sin, cos of n0 theta
+  double s1, c1;  // sin, cos of theta
+};
+
+__device__ __forceinline__ BasisStart basis_start(double r, double rc, int h) {
+  BasisStart b;
+  sincos(PI / rc * r, &b.s1, &b.c1);
+  double s = b.s1, c = b.c1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // 2^4 theta
+    const double s2 = 2.0 * s * c;
+    const double c2 = (c - s) * (c + s);
+    s = s2;
+    c = c2;
+  }
+  const double s17 = s * b.c1 + c * b.s1, c17 = c * b.c1 - s * b.s1;
+  b.s = h ? s17 : b.s1;
+  b.c = h ? c17 : b.c1;
+  return b;
+}
+
+// Basis functions n = n0 .. n0 + 15 of b_n = sin(n pi r / rc) / r * env(r / rc),
+// by the angle-addition recurrence in binary64 from a BasisStart; optionally
+// db_n / dr.
 template <bool DERIV>
-__device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16], float db[16]) {
-  const double theta = PI / rc * r;
-  double s1, c1, s, c;
-  sincos(theta, &s1, &c1);
-  sincos((double)n0 * theta, &s, &c);
+__device__ __forceinline__ void basis16_from(const BasisStart& st, double r, double rc, int n0,
+                                             float b[16], float db[16]) {
+  double s = st.s, c = st.c;
+  const double s1 = st.s1, c1 = st.c1;
   const double x = r / rc;
   const double env = envelope(x);
   const double inv_r = 1.0 / r;
@@ -112,6 +137,13 @@ __device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16]
     s = sn;
     c = cn;
   }
+}
+
+// Basis functions n0 = 16 h + 1 .. 16 h + 16 of a lane half h (and derivatives).
+template <bool DERIV>
+__device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16], float db[16]) {
+  const BasisStart st = basis_start(r, rc, n0 > 1 ? 1 : 0);
+  basis16_from<DERIV>(st, r, rc, n0, b, db);
 }
 
 // ---------------------------------------------------------------- harmonics

@@ -222,18 +222,19 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
       const int qq = valid ? q : qa;
       const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
       const Geo g = edge_geo(in, e);
-      f32x16 z1[2], z2[2], s2[2];
+      const BasisStart bst = basis_start(g.r, in.rc, h);
+      f32x16 d1[2], d2[2], s2[2];  // silu'(z1), silu'(z2), silu(z2)
       {
-        float bas[16];
-        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
-        layer1(w1s, bas, s, h, z1);
+        f32x16 z[2], s1[2];
+        {
+          float bas[16];
+          basis16_from<false>(bst, g.r, in.rc, 16 * h + 1, bas, nullptr);
+          layer1(w1s, bas, s, h, z);
+        }
+        silu_and_deriv(z, s1, d1);
+        layer2(w2s, s1, s, h, z);
+        silu_and_deriv(z, s2, d2);  // edges on N
       }
-      {
-        f32x16 s1[2];
-        silu_tiles(z1, s1);
-        layer2(w2s, s1, s, h, z2);
-      }
-      silu_tiles(z2, s2);  // edges on N
       __builtin_amdgcn_sched_barrier(0);
       // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k]  (edges on M; lane column = lm)
       f32x16 yb = zero16();
@@ -279,7 +280,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sb[m][r] *= silu_d(z2[m][r]);  // z2bar
+        for (int r = 0; r < 16; ++r) sb[m][r] *= d2[m][r];  // z2bar
       f32x16 s1b[2];
       s1b[0] = zero16();
       s1b[1] = zero16();
@@ -293,7 +294,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s1b[m][r] *= silu_d(z1[m][r]);  // z1bar
+        for (int r = 0; r < 16; ++r) s1b[m][r] *= d1[m][r];  // z1bar
       f32x16 bb = zero16();
       const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;
 #pragma unroll
@@ -302,7 +303,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
       float rbar = 0.f;
       {
         float bas[16], dbas[16];
-        basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
+        basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);  // cheaper to redo than to keep live
 #pragma unroll
         for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
       }
