@@ -44,6 +44,14 @@ def test_basis_sine_orthogonality():
     assert np.allclose(G, np.eye(32) * RC / 2, atol=1e-4)
 
 
+def test_basis_node_counts():
+    # b_n has exactly n - 1 sign changes inside (0, rc): fixes the first index n = 1
+    r = np.linspace(1e-3, 0.99 * RC, 20001)  # last interior zero of b_32 is at 31/32 rc
+    b = M.radial_basis(r, RC)
+    changes = (np.diff(np.sign(b), axis=0) != 0).sum(axis=0)
+    assert np.array_equal(changes, np.arange(32))
+
+
 def test_basis_derivative_against_finite_differences():
     r = np.linspace(0.8, 5.99, 57)
     _, db = M.radial_basis(r, RC, deriv=True)
