@@ -17,11 +17,12 @@ eec_energy_forces: the radial weights R of every edge on matrix cores) is
 timed in the same run and reported under "variants".
 
 Also reported:
-  roofline      the dominant kernel (the streaming backward), its launch
-                duration measured with hipEvents recorded by the library on
-                the stream it launches on; its algorithmic flops (see
-                BWD_FLOP_PER_EDGE / BWD_FLOP_PER_UNIT; recomputation excluded)
-                over that duration, against the FP32 matrix peak;
+  roofline      the dominant kernel (one species, folded: the fused
+                forward+backward kernel; otherwise the streaming backward),
+                its launch duration measured with hipEvents recorded by the
+                library on the stream it launches on; its algorithmic flops
+                (dominant_kernel; recomputation excluded) over that duration,
+                against the FP32 matrix peak;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
                 (all receivers of the cell: their forward and force backward),
                 on the host cores.
@@ -47,6 +48,21 @@ PEAK_HBM_GBS = 8000.0
 #         (2 * 16 * 64 * 64 = 131,072).
 BWD_FLOP_PER_EDGE = {"direct": 45056 + 2304 + 2048, "folded": 2048 + 2048 + 8192 + 4096}
 BWD_FLOP_PER_UNIT = {"direct": 0, "folded": 2 * 16 * 64 * 64}
+# Forward of the folded path, for its one-species fused kernel (forward and
+# backward in one launch): per edge W1 (4,096) + W2 (8,192) + T = s2 Y^T
+# (2,048); per unit A = h T^T W3 (131,072).
+FOLD_FWD_FLOP_PER_EDGE = 4096 + 8192 + 2048
+FOLD_FWD_FLOP_PER_UNIT = 2 * 16 * 64 * 64
+
+
+def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int):
+    """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
+    if variant == "folded" and n_species == 1:
+        flop = ((FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges
+                + (FOLD_FWD_FLOP_PER_UNIT + BWD_FLOP_PER_UNIT["folded"]) * n_units)
+        return "k_fold_fused", "forward", flop
+    flop = BWD_FLOP_PER_EDGE[variant] * n_edges + BWD_FLOP_PER_UNIT[variant] * n_units
+    return ("k_backward" if variant == "direct" else "k_fold_backward"), "backward", flop
 WORKLOADS = {
     "D4096": "diamond 8x8x8 conventional cells, 4096 atoms, a=3.567 A, rc=6.0 A, 0.02 A noise, seed 0, C=64",
     "D512": "diamond 4x4x4 conventional cells, 512 atoms, rc=6.0 A, C=64",
@@ -192,7 +208,6 @@ def main() -> int:
     other = "direct" if args.variant == "folded" else "folded"
     o_ms, o_phase, o_energy = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
-    bwd_ms = phase_ms["backward"]
     # units with at least one edge: (receiver, sender species) pairs present in the graph
     rp = g.row_ptr.cpu().numpy()
     if cfg.model.n_species == 1:
@@ -202,10 +217,12 @@ def main() -> int:
         recv = np.repeat(np.arange(g.n_atoms), np.diff(rp))
         n_units = len(np.unique(recv.astype(np.int64) * cfg.model.n_species + cfg.species[col]))
 
-    def bwd_flop(variant):
-        return BWD_FLOP_PER_EDGE[variant] * E + BWD_FLOP_PER_UNIT[variant] * n_units
+    def roof(variant, phases):
+        kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units)
+        launch_ms = phases[phase]
+        return kernel, flop, launch_ms, flop / (launch_ms * 1e-3) / 1e12
 
-    achieved = bwd_flop(args.variant) / (bwd_ms * 1e-3) / 1e12
+    kernel, flop, launch_ms, achieved = roof(args.variant, phase_ms)
     out = {
         "metric": METRIC,
         "value": E / (ms_per_step * 1e-3),
@@ -221,16 +238,15 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "n_atoms": cfg.n_atoms,
                    "n_edges": E, "channels": cfg.model.channels, "n_species": cfg.model.n_species},
-        "roofline": {"bound": "mfma",
-                     "kernel": "k_backward" if args.variant == "direct" else "k_fold_backward",
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                     "flop_per_launch": bwd_flop(args.variant), "launch_ms": bwd_ms},
+                     "flop_per_launch": flop, "launch_ms": launch_ms},
         "variant": args.variant,
         "variants": {other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase,
                              "energy": o_energy,
-                             "backward_frac": bwd_flop(other) / (o_phase["backward"] * 1e-3) / 1e12
-                             / PEAK_FP32_MFMA_TFLOPS}},
+                             "roofline_kernel": roof(other, o_phase)[0],
+                             "roofline_frac": roof(other, o_phase)[3] / PEAK_FP32_MFMA_TFLOPS}},
         "phases_ms": phase_ms,
         "neighbors_ms": nb_ms,
         "energy": energy,

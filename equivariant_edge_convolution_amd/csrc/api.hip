@@ -264,12 +264,31 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   Box b{{box[0], box[1], box[2]}};
   float* Rc = (float*)(ws + p.off_R);
   float* Yc = (float*)(ws + p.off_Y);
+  float* gbuf = (float*)(ws + p.off_g);
+  const bool folded = variant == EEC_VARIANT_FOLDED;
+  if (folded && fold_fused_supported(p)) {
+    // one kernel per receiver from geometry to dE/dd; no preparation, no A
+    mark(2 * EEC_PHASE_PREPARE);
+    launch_transpose_w3(s, p, m, ws);
+    mark(2 * EEC_PHASE_PREPARE + 1);
+    mark(2 * EEC_PHASE_FORWARD);
+    launch_fold_fused(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws);
+    mark(2 * EEC_PHASE_FORWARD + 1);
+    mark(2 * EEC_PHASE_READOUT);
+    launch_energy_total(s, p, ei, energy);
+    mark(2 * EEC_PHASE_READOUT + 1);
+    mark(2 * EEC_PHASE_BACKWARD);
+    mark(2 * EEC_PHASE_BACKWARD + 1);
+    mark(2 * EEC_PHASE_SCATTER);
+    launch_scatter(s, p, g, pos, b, gbuf, forces, (double*)(ws + p.off_vpart), virial);
+    mark(2 * EEC_PHASE_SCATTER + 1);
+    return launched("energy_forces");
+  }
   mark(2 * EEC_PHASE_PREPARE);
   launch_prepare(s, p, g, species, ws, A);
   mark(2 * EEC_PHASE_PREPARE + 1);
   mark(2 * EEC_PHASE_FORWARD);
   int nparts = 1;
-  const bool folded = variant == EEC_VARIANT_FOLDED;
   if (folded) {
     launch_fold_forward(s, p, g, pos, b, m->cutoff, species, m, A, ws);  // S partial slabs
     nparts = p.S;
@@ -287,7 +306,6 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   mark(2 * EEC_PHASE_READOUT);
   launch_readout(s, p, m, A, nparts, ei, energy);  // slab 0 of A now holds dE/dA
   mark(2 * EEC_PHASE_READOUT + 1);
-  float* gbuf = (float*)(ws + p.off_g);
   mark(2 * EEC_PHASE_BACKWARD);
   if (folded)
     launch_fold_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);

@@ -160,9 +160,10 @@ struct Geo {
   int i, j;
 };
 
-__device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) {
+// Edge e whose receiver the caller already knows (the unit's own atom).
+__device__ __forceinline__ Geo edge_geo_at(const EdgeIn& in, int64_t e, int i) {
   Geo g;
-  int i = in.recv[e], j = in.col[e];
+  int j = in.col[e];
   i = min(max(i, 0), in.n_atoms - 1);
   j = min(max(j, 0), in.n_atoms - 1);
   double d[3];
@@ -179,6 +180,8 @@ __device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) {
   g.j = j;
   return g;
 }
+
+__device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) { return edge_geo_at(in, e, in.recv[e]); }
 
 
 // Work units of the receiver-aligned kernels: (ordered species pair p, receiver i).

@@ -490,6 +490,10 @@ void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float*
   k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
 }
 
+void launch_energy_total(hipStream_t s, const ConvPlan& p, const float* ei, float* energy) {
+  k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
+}
+
 void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                     const float* gin, float* forces, double* vpart, float* virial) {
   if (p.N == 0) {

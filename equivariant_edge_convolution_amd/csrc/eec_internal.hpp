@@ -96,10 +96,24 @@ void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box,
 // slabs; backward (also writes the transposed last-layer weights it reads).
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                          Box box, double cutoff, const int32_t* species, const eec_model* m,
-                         float* A_out, const char* ws);
+                         float* A_out, char* ws);
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                           Box box, double cutoff, const int32_t* species, const eec_model* m,
                           const float* Abar, float* gout, char* ws);
+
+// W3T[p][j][k] = W3[p][k][j] into the workspace (read by the folded backward).
+void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);
+
+// One species: the whole folded call per receiver in one kernel (forward tiles,
+// A_i, E_i into ei, dE/dA_i, backward tiles into gout).  Reads the transposed
+// last-layer weights launch_transpose_w3 wrote.
+bool fold_fused_supported(const ConvPlan& p);
+void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
+                       char* ws);
+
+// E = sum_i ei[i] (binary64, fixed order).
+void launch_energy_total(hipStream_t s, const ConvPlan& p, const float* ei, float* energy);
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

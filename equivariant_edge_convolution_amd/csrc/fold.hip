@@ -20,17 +20,137 @@ namespace eec {
 namespace {
 using namespace chain;
 
+// ------------------------------------------------------------------ per-wave LDS
+// Every unit belongs to one wave; its LDS region holds, in turn,
+//   forward:  ysm [32][17] harmonics of the tile's edges (zero rows for padding),
+//             tsm [64][16] T of the unit, staged for the last layer;
+//   backward: ahsm [C][AHS] dE/dA_{lm,c} h_c by channel row, then (written once
+//             every ahsm row has been read) msm [16][65] M of the unit, and
+//             ybsm [32][17] dE/dY of the tile's edges.
+constexpr int AHS = NLM + 4;  // row stride of the staged dE/dA h rows (16-byte aligned)
+template <int C>
+struct FoldLds {
+  static constexpr int YSM = 0, TSM = 32 * (NLM + 1), FWD = TSM + HID * NLM;
+  static constexpr int AHSM = 0, MSM = 0, YBSM = NLM * (HID + 1), BWD_M = YBSM + 32 * (NLM + 1);
+  static constexpr int BWD = C * AHS > BWD_M ? C * AHS : BWD_M;
+  static constexpr int FWD_ONLY = FWD, BWD_ONLY = BWD, FUSED = FWD > BWD ? FWD : BWD;
+};
+
+template <int C>
+struct WaveLds {
+  float (*ysm)[NLM + 1];
+  float (*tsm)[NLM];
+  float (*ahsm)[AHS];
+  float (*msm)[HID + 1];
+  float (*ybsm)[NLM + 1];
+  __device__ explicit WaveLds(float* base) {
+    ysm = reinterpret_cast<float (*)[NLM + 1]>(base + FoldLds<C>::YSM);
+    tsm = reinterpret_cast<float (*)[NLM]>(base + FoldLds<C>::TSM);
+    ahsm = reinterpret_cast<float (*)[AHS]>(base + FoldLds<C>::AHSM);
+    msm = reinterpret_cast<float (*)[HID + 1]>(base + FoldLds<C>::MSM);
+    ybsm = reinterpret_cast<float (*)[NLM + 1]>(base + FoldLds<C>::YBSM);
+  }
+};
+
 // ------------------------------------------------------------------ forward
+// One 32-edge tile [q0, q0 + 32) of unit (p, i) (positions in the work order,
+// `perm` maps them to CSR edges; NULL = identity): T += s2^T Y over the tile.
+__device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const float* w1s,
+                                         const float* w2s, float (*ysm)[NLM + 1], int i, int q0,
+                                         int qa, int qb, int s, int h, f32x16 T[2]) {
+  const int q = q0 + s;
+  const bool valid = q < qb;
+  const int qq = valid ? q : qa;
+  const int64_t e = perm ? (int64_t)perm[qq] : (int64_t)qq;
+  const Geo g = edge_geo_at(in, e, i);
+  f32x16 z[2], a[2];
+  {
+    float bas[16];
+    basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+    layer1(w1s, bas, s, h, z);
+  }
+  silu_tiles(z, a);  // s1, edges on N
+  // z2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s
+  {
+    const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
+    z[0] = zero16();
+    z[1] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      const float av = a[ks >> 4][ks & 15];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) z[m] = mfma32(av, w[hid_k0(ks) * LDH + 32 * m], z[m]);
+    }
+  }
+  silu_tiles(z, a);  // s2, edges on M
+  {
+    float Y[16];
+    sph16(g.ux, g.uy, g.uz, Y);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ysm[s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
+  }
+  wave_sync_lds();
+  // T[hidden][lm] += sum over this tile's edges (K = edges, pairs (fperm(ks), fperm(ks)+4))
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const float yv = s < NLM ? ysm[fperm(ks) + 4 * h][s] : 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) T[m] = mfma32(a[m][ks], yv, T[m]);
+  }
+  wave_sync_lds();
+}
+
+// T of the unit to LDS, then acc[q][lm] = sum_k T[k][lm] W3[k][l(lm) C + c]
+// for channel c = lane + 64 q (the h_c factor is the caller's).
+template <int C>
+__device__ __forceinline__ void unit_last_layer(const f32x16 T[2], float (*tsm)[NLM], const float* w3,
+                                                int lane, int s, int h, float acc[C / 64][NLM]) {
+  constexpr int NC = 4 * C, CPL = C / 64;
+  // T register r of tile m, lane (s, h): hidden 32 m + fperm(r) + 4h, harmonic s (< 16)
+  if (s < NLM) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tsm[32 * m + fperm(r) + 4 * h][s] = T[m][r];
+  }
+  wave_sync_lds();
+#pragma unroll
+  for (int q = 0; q < CPL; ++q)
+#pragma unroll
+    for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < HID; ++k) {
+    float t[NLM];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(&tsm[k][4 * v]);
+      t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
+    }
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const float* wr = w3 + (size_t)k * NC + lane + 64 * q;
+      const float w0 = wr[0], wl1 = wr[C], wl2 = wr[2 * C], wl3 = wr[3 * C];
+      acc[q][0] += t[0] * w0;
+#pragma unroll
+      for (int lm = 1; lm < 4; ++lm) acc[q][lm] += t[lm] * wl1;
+#pragma unroll
+      for (int lm = 4; lm < 9; ++lm) acc[q][lm] += t[lm] * wl2;
+#pragma unroll
+      for (int lm = 9; lm < 16; ++lm) acc[q][lm] += t[lm] * wl3;
+    }
+  }
+  wave_sync_lds();  // every tsm read done before the region is reused
+}
+
 template <int C, int W>
 __global__ void __launch_bounds__(64 * W)
 k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
                const float* __restrict__ W3, const float* __restrict__ emb, float* __restrict__ A_out) {
-  constexpr int NC = 4 * C, CPL = C / 64;
+  constexpr int CPL = C / 64;
   __shared__ float w12[W12_FLOATS];
-  __shared__ float ysm[W][32][NLM + 1];  // harmonics of the tile's edges (zero rows for padding)
-  __shared__ float tsm[W][HID][NLM];     // T of the unit, staged for the last layer
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::FWD_ONLY];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lane_s = lane & 31, lane_h = lane >> 5;
+  const WaveLds<C> L(wbuf[wave]);
   const float* w1s = w12;
   const float* w2s = w12 + NB * LDH;
   const int N = un.n_atoms, S = un.S, P = S * S;
@@ -47,90 +167,15 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
     const int i = (b - p * nbp) * W + wave;
     int qa, qb;
     if (i >= N || !unit_range(un, p, i, qa, qb)) continue;
-    int s = lane_s, h = lane_h;
+    int s = lane & 31, h = lane >> 5;
     asm volatile("" : "+v"(s), "+v"(h));
     const int zs = p % S;
     f32x16 T[2];
     T[0] = zero16();
     T[1] = zero16();
-    for (int q0 = qa; q0 < qb; q0 += 32) {
-      const int q = q0 + s;
-      const bool valid = q < qb;
-      const int qq = valid ? q : qa;
-      const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
-      const Geo g = edge_geo(in, e);
-      f32x16 z[2], a[2];
-      {
-        float bas[16];
-        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
-        layer1(w1s, bas, s, h, z);
-      }
-      silu_tiles(z, a);  // s1, edges on N
-      // z2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s
-      {
-        const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
-        z[0] = zero16();
-        z[1] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-          const float av = a[ks >> 4][ks & 15];
-#pragma unroll
-          for (int m = 0; m < 2; ++m) z[m] = mfma32(av, w[hid_k0(ks) * LDH + 32 * m], z[m]);
-        }
-      }
-      silu_tiles(z, a);  // s2, edges on M
-      {
-        float Y[16];
-        sph16(g.ux, g.uy, g.uz, Y);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ysm[wave][s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
-      }
-      wave_sync_lds();
-      // T[hidden][lm] += sum over this tile's edges (K = edges, pairs (fperm(ks), fperm(ks)+4))
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const float yv = s < NLM ? ysm[wave][fperm(ks) + 4 * h][s] : 0.f;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) T[m] = mfma32(a[m][ks], yv, T[m]);
-      }
-      wave_sync_lds();
-    }
-    // T register r of tile m, lane (s, h): hidden 32 m + fperm(r) + 4h, harmonic s (< 16)
-    if (s < NLM) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tsm[wave][32 * m + fperm(r) + 4 * h][s] = T[m][r];
-    }
-    wave_sync_lds();
-    // A[lm][c] = h_c sum_k T[k][lm] W3[k][l(lm) C + c]; lane = channel(s)
-    const float* w3 = W3 + (size_t)p * HID * NC;
+    for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, un.perm, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
     float acc[CPL][NLM];
-#pragma unroll
-    for (int q = 0; q < CPL; ++q)
-#pragma unroll
-      for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < HID; ++k) {
-      float t[NLM];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float4 x = *reinterpret_cast<const float4*>(&tsm[wave][k][4 * v]);
-        t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
-      }
-#pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const float* wr = w3 + (size_t)k * NC + lane + 64 * q;
-        const float w0 = wr[0], wl1 = wr[C], wl2 = wr[2 * C], wl3 = wr[3 * C];
-        acc[q][0] += t[0] * w0;
-#pragma unroll
-        for (int lm = 1; lm < 4; ++lm) acc[q][lm] += t[lm] * wl1;
-#pragma unroll
-        for (int lm = 4; lm < 9; ++lm) acc[q][lm] += t[lm] * wl2;
-#pragma unroll
-        for (int lm = 9; lm < 16; ++lm) acc[q][lm] += t[lm] * wl3;
-      }
-    }
+    unit_last_layer<C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, s, h, acc);
     float* ao = A_out + ((size_t)zs * N + i) * NLM * C;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -139,12 +184,144 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
 #pragma unroll
       for (int k = 0; k < NLM; ++k) ao[k * C + c] = hc * acc[q][k];
     }
-    wave_sync_lds();
   }
 }
 
 // ------------------------------------------------------------------ backward
-constexpr int AHS = NLM + 4;  // row stride of the staged Abar h rows (16-byte aligned)
+// M[lm][k] = sum_c (dE/dA h)[lm][c] W3[k][l(lm) C + c] from the staged ahsm rows
+// (lane = hidden k; wt = W3T of the pair + lane), into msm over the ahsm region.
+template <int C>
+__device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int lane, float (*msm)[HID + 1]) {
+  float macc[NLM];
+#pragma unroll
+  for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < C; ++c) {
+    float av[NLM];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(&ahsm[c][4 * v]);
+      av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
+    }
+    const float w0 = wt[(size_t)c * HID], wl1 = wt[(size_t)(C + c) * HID];
+    const float wl2 = wt[(size_t)(2 * C + c) * HID], wl3 = wt[(size_t)(3 * C + c) * HID];
+    macc[0] += av[0] * w0;
+#pragma unroll
+    for (int lm = 1; lm < 4; ++lm) macc[lm] += av[lm] * wl1;
+#pragma unroll
+    for (int lm = 4; lm < 9; ++lm) macc[lm] += av[lm] * wl2;
+#pragma unroll
+    for (int lm = 9; lm < 16; ++lm) macc[lm] += av[lm] * wl3;
+  }
+  wave_sync_lds();  // msm overlays ahsm
+#pragma unroll
+  for (int lm = 0; lm < NLM; ++lm) msm[lm][lane] = macc[lm];
+  wave_sync_lds();
+}
+
+// One 32-edge tile of the backward of unit (p, i): g = dE/dd of its edges.
+__device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, const float* w1s,
+                                         const float* w2s, float (*msm)[HID + 1], float (*ybsm)[NLM + 1],
+                                         int i, int q0, int qa, int qb, int s, int h,
+                                         float* __restrict__ gout) {
+  const int q = q0 + s;
+  const bool valid = q < qb;
+  const int qq = valid ? q : qa;
+  const int64_t e = perm ? (int64_t)perm[qq] : (int64_t)qq;
+  const Geo g = edge_geo_at(in, e, i);
+  f32x16 d1[2], d2[2], s2[2];  // silu'(z1), silu'(z2), silu(z2); edges on N
+  {
+    f32x16 z[2], s1[2];
+    {
+      float bas[16];
+      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+      layer1(w1s, bas, s, h, z);
+    }
+    silu_and_deriv(z, s1, d1);
+    layer2(w2s, s1, s, h, z);
+    silu_and_deriv(z, s2, d2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k]  (edges on M; lane column = lm)
+  f32x16 yb = zero16();
+  {
+    const float* mr = &msm[s < NLM ? s : 0][4 * h];
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      const float bv = s < NLM ? mr[hid_k0(ks)] : 0.f;
+      yb = mfma32(s2[ks >> 4][ks & 15], bv, yb);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // s2bar[k][edge] = sum_lm M[lm][k] Y[edge][lm]  (edges on N; K pairs (2ks, 2ks + 1))
+  f32x16 sb[2];
+  sb[0] = zero16();
+  sb[1] = zero16();
+  {
+    float Y[16];
+    sph16(g.ux, g.uy, g.uz, Y);
+    const float* mc = &msm[h][s];  // M[2 ks + h][32 m + s]
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float bv = h ? Y[2 * ks + 1] : Y[2 * ks];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) sb[m] = mfma32(mc[2 * ks * (HID + 1) + 32 * m], bv, sb[m]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Ybar to the lanes that own the edges, contracted with the harmonic gradients
+  if (s < NLM) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ybsm[fperm(r) + 4 * h][s] = yb[r];
+  }
+  wave_sync_lds();
+  float G[3];
+  {
+    float ybe[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ybe[k] = ybsm[s][k];
+    sph16_grad_dot(g.ux, g.uy, g.uz, ybe, G);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[m][r] *= d2[m][r];  // z2bar
+  f32x16 s1b[2];
+  s1b[0] = zero16();
+  s1b[1] = zero16();
+  const float* w2c = w2s + s * LDH + 4 * h;  // W2[32 m + s][hid_k0(ks) + 4 h]
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) {
+    const float bv = sb[ks >> 4][ks & 15];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) s1b[m] = mfma32(w2c[32 * m * LDH + hid_k0(ks)], bv, s1b[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1b[m][r] *= d1[m][r];  // z1bar
+  f32x16 bb = zero16();
+  const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) bb = mfma32(w1c[hid_k0(ks)], s1b[ks >> 4][ks & 15], bb);
+  __builtin_amdgcn_sched_barrier(0);
+  float rbar = 0.f;
+  {
+    float bas[16], dbas[16];
+    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);  // cheaper to redo than to keep live
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
+  }
+  rbar += __shfl_xor(rbar, 32);
+  const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
+  if (valid && h == 0) {
+    gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
+    gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
+    gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+  }
+  wave_sync_lds();
+}
 
 template <int C, int W>
 __global__ void __launch_bounds__(64 * W)
@@ -153,11 +330,9 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
                 const float* __restrict__ Abar, float* __restrict__ gout) {
   constexpr int NC = 4 * C, CPL = C / 64;
   __shared__ float w12[W12_FLOATS];
-  __shared__ float ahsm[W][C][AHS];         // Abar_{lm,c} h_c, row c
-  __shared__ float msm[W][NLM][HID + 1];    // M_{lm,k}
-  __shared__ float ybsm[W][32][NLM + 1];    // Ybar of the tile, row = edge slot
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::BWD_ONLY];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lane_s = lane & 31, lane_h = lane >> 5;
+  const WaveLds<C> L(wbuf[wave]);
   const float* w1s = w12;
   const float* w2s = w12 + NB * LDH;
   const int N = un.n_atoms, S = un.S, P = S * S;
@@ -174,7 +349,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
     const int i = (b - p * nbp) * W + wave;
     int qa, qb;
     if (i >= N || !unit_range(un, p, i, qa, qb) || qb <= qa) continue;
-    int s = lane_s, h = lane_h;
+    int s = lane & 31, h = lane >> 5;
     asm volatile("" : "+v"(s), "+v"(h));
     const int zs = p % S;
     // stage Abar_i h_s (lane = channel)
@@ -184,138 +359,73 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
       const float hc = emb[(size_t)zs * C + c];
       const float* ar = Abar + (size_t)i * NLM * C + c;
 #pragma unroll
-      for (int lm = 0; lm < NLM; ++lm) ahsm[wave][c][lm] = ar[lm * C] * hc;
+      for (int lm = 0; lm < NLM; ++lm) L.ahsm[c][lm] = ar[lm * C] * hc;
     }
     wave_sync_lds();
-    // M[lm][k] = sum_c Abar h [lm][c] W3[k][l(lm) C + c]; lane = hidden k
-    {
-      const float* wt = W3T + (size_t)p * NC * HID + lane;  // W3T[p][j][k] = W3[p][k][j]
-      float macc[NLM];
-#pragma unroll
-      for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < C; ++c) {
-        float av[NLM];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4 x = *reinterpret_cast<const float4*>(&ahsm[wave][c][4 * v]);
-          av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
-        }
-        const float w0 = wt[(size_t)c * HID], wl1 = wt[(size_t)(C + c) * HID];
-        const float wl2 = wt[(size_t)(2 * C + c) * HID], wl3 = wt[(size_t)(3 * C + c) * HID];
-        macc[0] += av[0] * w0;
-#pragma unroll
-        for (int lm = 1; lm < 4; ++lm) macc[lm] += av[lm] * wl1;
-#pragma unroll
-        for (int lm = 4; lm < 9; ++lm) macc[lm] += av[lm] * wl2;
-#pragma unroll
-        for (int lm = 9; lm < 16; ++lm) macc[lm] += av[lm] * wl3;
-      }
-#pragma unroll
-      for (int lm = 0; lm < NLM; ++lm) msm[wave][lm][lane] = macc[lm];
-    }
-    wave_sync_lds();
+    unit_M<C>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      bwd_tile(in, un.perm, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
+  }
+}
 
-    for (int q0 = qa; q0 < qb; q0 += 32) {
-      const int q = q0 + s;
-      const bool valid = q < qb;
-      const int qq = valid ? q : qa;
-      const int64_t e = un.perm ? (int64_t)un.perm[qq] : (int64_t)qq;
-      const Geo g = edge_geo(in, e);
-      const BasisStart bst = basis_start(g.r, in.rc, h);
-      f32x16 d1[2], d2[2], s2[2];  // silu'(z1), silu'(z2), silu(z2)
-      {
-        f32x16 z[2], s1[2];
-        {
-          float bas[16];
-          basis16_from<false>(bst, g.r, in.rc, 16 * h + 1, bas, nullptr);
-          layer1(w1s, bas, s, h, z);
-        }
-        silu_and_deriv(z, s1, d1);
-        layer2(w2s, s1, s, h, z);
-        silu_and_deriv(z, s2, d2);  // edges on N
+// ------------------------------------------------------------------ fused (one species)
+// With one species, receiver i's unit holds its whole row, and the backward of
+// the unit needs only M_i, which depends on nothing but the unit's own forward:
+// one wave runs forward tiles -> A_i -> E_i and dE/dA_i h -> M_i -> backward
+// tiles, so A never leaves the chip and the readout needs no kernel of its own.
+// (The forward's activations are recomputed in the backward tiles: keeping them
+// would cost a round trip of 3 x 64 floats per edge through HBM, more than the
+// two layers take to redo.)
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
+             const float* __restrict__ W3, const float* __restrict__ W3T, const float* __restrict__ emb,
+             const float* __restrict__ w_read, float* __restrict__ ei, float* __restrict__ gout) {
+  constexpr int CPL = C / 64;
+  __shared__ float w12[W12_FLOATS];
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const WaveLds<C> L(wbuf[wave]);
+  const float* w1s = w12;
+  const float* w2s = w12 + NB * LDH;
+  const int N = un.n_atoms;
+  const int nbp = (N + W - 1) / W;
+  stage_w12(w12, W1, W2, 0);
+  __syncthreads();
+  for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
+    const int i = b * W + wave;
+    if (i >= N) continue;
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
+    f32x16 T[2];
+    T[0] = zero16();
+    T[1] = zero16();
+    for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, nullptr, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
+    float acc[CPL][NLM];
+    unit_last_layer<C>(T, L.tsm, W3, lane, s, h, acc);
+    // E_i = sum_c w_c sum_lm A^2 and dE/dA h = 2 w_c A h_c, A = h_c acc
+    float esum = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c = lane + 64 * q;
+      const float hc = emb[c], wc = w_read[c];
+      float sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) {
+        const float av = hc * acc[q][k];
+        sq += av * av;
+        L.ahsm[c][k] = 2.f * wc * av * hc;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k]  (edges on M; lane column = lm)
-      f32x16 yb = zero16();
-      {
-        const float* mr = &msm[wave][s < NLM ? s : 0][4 * h];
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-          const float bv = s < NLM ? mr[hid_k0(ks)] : 0.f;
-          yb = mfma32(s2[ks >> 4][ks & 15], bv, yb);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // s2bar[k][edge] = sum_lm M[lm][k] Y[edge][lm]  (edges on N; K pairs (2ks, 2ks + 1))
-      f32x16 sb[2];
-      sb[0] = zero16();
-      sb[1] = zero16();
-      {
-        float Y[16];
-        sph16(g.ux, g.uy, g.uz, Y);
-        const float* mc = &msm[wave][h][s];  // M[2 ks + h][32 m + s]
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const float bv = h ? Y[2 * ks + 1] : Y[2 * ks];
-#pragma unroll
-          for (int m = 0; m < 2; ++m) sb[m] = mfma32(mc[2 * ks * (HID + 1) + 32 * m], bv, sb[m]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Ybar to the lanes that own the edges, contracted with the harmonic gradients
-      if (s < NLM) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ybsm[wave][fperm(r) + 4 * h][s] = yb[r];
-      }
-      wave_sync_lds();
-      float G[3];
-      {
-        float ybe[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) ybe[k] = ybsm[wave][s][k];
-        sph16_grad_dot(g.ux, g.uy, g.uz, ybe, G);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sb[m][r] *= d2[m][r];  // z2bar
-      f32x16 s1b[2];
-      s1b[0] = zero16();
-      s1b[1] = zero16();
-      const float* w2c = w2s + s * LDH + 4 * h;  // W2[32 m + s][hid_k0(ks) + 4 h]
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        const float bv = sb[ks >> 4][ks & 15];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) s1b[m] = mfma32(w2c[32 * m * LDH + hid_k0(ks)], bv, s1b[m]);
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s1b[m][r] *= d1[m][r];  // z1bar
-      f32x16 bb = zero16();
-      const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) bb = mfma32(w1c[hid_k0(ks)], s1b[ks >> 4][ks & 15], bb);
-      __builtin_amdgcn_sched_barrier(0);
-      float rbar = 0.f;
-      {
-        float bas[16], dbas[16];
-        basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);  // cheaper to redo than to keep live
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
-      }
-      rbar += __shfl_xor(rbar, 32);
-      const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
-      if (valid && h == 0) {
-        gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
-        gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
-        gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
-      }
-      wave_sync_lds();
+      esum += wc * sq;
     }
+    for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
+    if (lane == 0) ei[i] = esum;
+    if (qb <= qa) continue;
+    wave_sync_lds();
+    unit_M<C>(L.ahsm, W3T + lane, lane, L.msm);
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      bwd_tile(in, nullptr, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
   }
 }
 
@@ -332,14 +442,14 @@ __global__ void k_transpose_w3(int P, int NC, const float* __restrict__ W3, floa
 constexpr int WAVES = 8;
 
 EdgeIn make_in_f(const ConvPlan& p, const eec_graph* g, const double* pos, Box box, double cutoff,
-                 const int32_t* species, const char* ws) {
+                 const int32_t* species) {
   EdgeIn in;
   in.pos = pos;
   in.Lx = box.L[0];
   in.Ly = box.L[1];
   in.Lz = box.L[2];
   in.rc = cutoff;
-  in.recv = (const int32_t*)(ws + p.off_recv);
+  in.recv = nullptr;  // the unit kernels know each edge's receiver
   in.col = g->col;
   in.shift = g->shift;
   in.species = species;
@@ -368,9 +478,9 @@ int unit_grid(const ConvPlan& p) {
 
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                          Box box, double cutoff, const int32_t* species, const eec_model* m,
-                         float* A_out, const char* ws) {
+                         float* A_out, char* ws) {
   if (p.N == 0) return;
-  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species, ws);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
   if (p.C == 64)
     k_fold_forward<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, m->emb, A_out);
@@ -378,14 +488,34 @@ void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, c
     k_fold_forward<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, m->emb, A_out);
 }
 
+void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws) {
+  float* W3T = (float*)(ws + p.off_w3t);
+  const int64_t n = (int64_t)p.P * HID * p.NC;
+  k_transpose_w3<<<(int)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, s>>>(p.P, p.NC, m->W3, W3T);
+}
+
+bool fold_fused_supported(const ConvPlan& p) { return p.S == 1; }
+
+void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
+                       char* ws) {
+  if (p.N == 0) return;
+  const float* W3T = (const float*)(ws + p.off_w3t);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
+  const Units un = make_units(p, g, species, ws);
+  if (p.C == 64)
+    k_fold_fused<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ei, gout);
+  else
+    k_fold_fused<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ei, gout);
+}
+
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                           Box box, double cutoff, const int32_t* species, const eec_model* m,
                           const float* Abar, float* gout, char* ws) {
   if (p.N == 0 || p.E == 0) return;
-  float* W3T = (float*)(ws + p.off_w3t);
-  const int64_t n = (int64_t)p.P * HID * p.NC;
-  k_transpose_w3<<<(int)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, s>>>(p.P, p.NC, m->W3, W3T);
-  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species, ws);
+  launch_transpose_w3(s, p, m, ws);
+  const float* W3T = (const float*)(ws + p.off_w3t);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
   if (p.C == 64)
     k_fold_backward<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, W3T, m->emb, Abar, gout);

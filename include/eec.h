@@ -211,7 +211,9 @@ EEC_API eec_status eec_energy_forces(void *stream, const eec_graph *g, const dou
  *             A_i[lm][c] = sum_s h_{s,c} sum_k T_{i,s}[k][lm] W3_{(Z_i,s)}[k][l C + c];
  *   backward: M_{i,s}[lm][k] = sum_c (dE/dA_i)[lm][c] h_{s,c} W3_{(Z_i,s)}[k][l C + c],
  *             dE/dY_e = M s2_e,  dE/ds2_e = M^T Y_e.
- * The per-edge radial weights R are never formed.  Arguments as
+ * The per-edge radial weights R are never formed.  With one species the
+ * whole call per receiver (forward tiles, A_i, E_i, dE/dA_i, backward tiles)
+ * runs in one kernel and A never leaves the chip.  Arguments as
  * eec_energy_forces; same workspace size. */
 EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, const double *pos,
                                     const double *box /*[host][3]*/, const int32_t *species,
@@ -224,12 +226,17 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * eec_energy_forces_folded (EEC_VARIANT_FOLDED), with hipEvent_t handles
  * (created by the caller, e.g. with hipEventCreate) recorded on `stream` around
  * each phase: events[2k] before and events[2k+1] after phase k, for
- *   k = EEC_PHASE_PREPARE   receiver index and pair grouping,
+ *   k = EEC_PHASE_PREPARE   receiver index and pair grouping (folded, one
+ *                           species: the transpose of W3 only),
  *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
- *                           radial-row chunks and message passes),
- *       EEC_PHASE_READOUT   per-atom energies, dE/dA, total energy,
+ *                           radial-row chunks and message passes; folded,
+ *                           one species: the single fused kernel launch,
+ *                           forward and backward),
+ *       EEC_PHASE_READOUT   per-atom energies, dE/dA, total energy (folded,
+ *                           one species: the total energy only),
  *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch; the
- *                           folded variant also transposes W3 first),
+ *                           folded variant also transposes W3 first; folded,
+ *                           one species: empty),
  *       EEC_PHASE_SCATTER   forces (and virial).
  * `events` holds 2 * EEC_N_PHASES handles; NULL records nothing.  Results are
  * bit for bit those of the untimed call. */
