@@ -269,18 +269,17 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   if (folded && fold_fused_supported(p)) {
     // one kernel per receiver from geometry to dE/dd; no preparation, no A
     mark(2 * EEC_PHASE_PREPARE);
-    launch_transpose_w3(s, p, m, ws);
+    if (fold_fused_needs_w3t(p)) launch_transpose_w3(s, p, m, ws);
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);
     launch_fold_fused(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws);
     mark(2 * EEC_PHASE_FORWARD + 1);
-    mark(2 * EEC_PHASE_READOUT);
-    launch_energy_total(s, p, ei, energy);
-    mark(2 * EEC_PHASE_READOUT + 1);
-    mark(2 * EEC_PHASE_BACKWARD);
-    mark(2 * EEC_PHASE_BACKWARD + 1);
+    for (int k : {EEC_PHASE_READOUT, EEC_PHASE_BACKWARD}) {
+      mark(2 * k);
+      mark(2 * k + 1);
+    }
     mark(2 * EEC_PHASE_SCATTER);
-    launch_scatter(s, p, g, pos, b, gbuf, forces, (double*)(ws + p.off_vpart), virial);
+    launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
     mark(2 * EEC_PHASE_SCATTER + 1);
     return launched("energy_forces");
   }
@@ -304,7 +303,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   }
   mark(2 * EEC_PHASE_FORWARD + 1);
   mark(2 * EEC_PHASE_READOUT);
-  launch_readout(s, p, m, A, nparts, ei, energy);  // slab 0 of A now holds dE/dA
+  launch_readout(s, p, m, A, nparts, ei);  // slab 0 of A now holds dE/dA
   mark(2 * EEC_PHASE_READOUT + 1);
   mark(2 * EEC_PHASE_BACKWARD);
   if (folded)
@@ -313,7 +312,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     launch_backward(s, p, g, pos, b, m->cutoff, species, m, A, gbuf, ws);
   mark(2 * EEC_PHASE_BACKWARD + 1);
   mark(2 * EEC_PHASE_SCATTER);
-  launch_scatter(s, p, g, pos, b, gbuf, forces, (double*)(ws + p.off_vpart), virial);
+  launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
   mark(2 * EEC_PHASE_SCATTER + 1);
   return launched("energy_forces");
 }

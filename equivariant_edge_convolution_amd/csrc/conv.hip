@@ -23,13 +23,14 @@ inline int blocks_for(int64_t n, int per) {
 __global__ void __launch_bounds__(256) k_recv(int32_t n, const int32_t* __restrict__ rp,
                                               int64_t E, int32_t* __restrict__ recv,
                                               float* __restrict__ A, int C) {
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
-  if (i >= n) return;
-  const int a = max(0, min(rp[i], (int)E)), b = max(a, min(rp[i + 1], (int)E));
-  for (int e = a + lane; e < b; e += 64) recv[e] = i;
-  if (A != nullptr && a == b)
-    for (int k = lane; k < NLM * C; k += 64) A[(size_t)i * NLM * C + k] = 0.f;
+  for (int i = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < n;
+       i += (int)((gridDim.x * blockDim.x) >> 6)) {
+    const int a = max(0, min(rp[i], (int)E)), b = max(a, min(rp[i + 1], (int)E));
+    for (int e = a + lane; e < b; e += 64) recv[e] = i;
+    if (A != nullptr && a == b)
+      for (int k = lane; k < NLM * C; k += 64) A[(size_t)i * NLM * C + k] = 0.f;
+  }
 }
 
 constexpr int PB = 1024;  // edges per counting block
@@ -275,39 +276,60 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, int nparts, const fl
   if (lane == 0) ei[i] = sum;
 }
 
-// E = sum_i E_i in binary64, one workgroup, contiguous thread slices then a tree.
-__global__ void __launch_bounds__(1024) k_energy_total(int32_t n, const float* __restrict__ ei,
-                                                       float* __restrict__ energy) {
-  __shared__ double part[1024];
+// ------------------------------------------------------------ totals
+// Totals of one 256-thread workgroup, in binary64 with a fixed order: each
+// thread a contiguous slice of atoms, then a tree.  E = sum_i E_i; with VIRIAL,
+// W = sum_i vpart_i.
+constexpr int TT = 256;
+template <bool VIRIAL>
+__device__ void block_totals(int32_t n, const float* __restrict__ ei, const double* __restrict__ vpart,
+                             float* __restrict__ energy, float* __restrict__ virial) {
+  constexpr int NT = VIRIAL ? 10 : 1;
+  __shared__ double part[NT][TT];
   const int t = threadIdx.x;
-  const int per = (n + 1023) / 1024;
+  const int per = (n + TT - 1) / TT;
   const int a = std::min(n, t * per), b = std::min(n, a + per);
-  double s = 0.0;
-  for (int k = a; k < b; ++k) s += (double)ei[k];
-  part[t] = s;
+  double acc[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) acc[k] = 0.0;
+  for (int i = a; i < b; ++i) {
+    acc[0] += (double)ei[i];
+    if (VIRIAL)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) acc[1 + k] += vpart[9 * (size_t)i + k];
+  }
+#pragma unroll
+  for (int k = 0; k < NT; ++k) part[k][t] = acc[k];
   __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (t < o) part[t] += part[t + o];
+  for (int o = TT / 2; o > 0; o >>= 1) {
+    if (t < o)
+#pragma unroll
+      for (int k = 0; k < NT; ++k) part[k][t] += part[k][t + o];
     __syncthreads();
   }
-  if (t == 0) energy[0] = (float)part[0];
+  if (t == 0) energy[0] = (float)part[0][0];
+  if (VIRIAL && t < 9) virial[t] = (float)part[1 + t][0];
+}
+
+// The totals alone (a cell without atoms: zeros).
+template <bool VIRIAL>
+__global__ void __launch_bounds__(TT) k_totals(int32_t n, const float* __restrict__ ei,
+                                               const double* __restrict__ vpart, float* __restrict__ energy,
+                                               float* __restrict__ virial) {
+  block_totals<VIRIAL>(n, ei, vpart, energy, virial);
 }
 
 // ------------------------------------------------------------ force scatter
 // One wave per atom: F_i = sum_{e in row i} (g_e - g_rev(e)); lanes take a fixed
-// stride of the row, then a fixed shuffle tree.  With `vpart`, also the atom's
+// stride of the row, then a fixed shuffle tree.  With VIRIAL, also the atom's
 // share of the virial -sum_e d_e g_e^T (in binary64).
 template <bool VIRIAL>
-__global__ void __launch_bounds__(256) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
-                                                 const int32_t* __restrict__ col,
-                                                 const int8_t* __restrict__ shift,
-                                                 const int32_t* __restrict__ rev,
-                                                 const double* __restrict__ pos, double Lx, double Ly,
-                                                 double Lz, const float* __restrict__ g,
-                                                 float* __restrict__ F, double* __restrict__ vpart) {
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (i >= n) return;
+__device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t E,
+                                             const int32_t* __restrict__ rp, const int32_t* __restrict__ col,
+                                             const int8_t* __restrict__ shift, const int32_t* __restrict__ rev,
+                                             const double* __restrict__ pos, double Lx, double Ly, double Lz,
+                                             const float* __restrict__ g, float* __restrict__ F,
+                                             double* __restrict__ vpart) {
   float fx = 0.f, fy = 0.f, fz = 0.f;
   double v[9];
 #pragma unroll
@@ -348,24 +370,27 @@ __global__ void __launch_bounds__(256) k_scatter(int32_t n, int64_t E, const int
   }
 }
 
-__global__ void __launch_bounds__(1024) k_virial_total(int32_t n, const double* __restrict__ vpart,
-                                                       float* __restrict__ virial) {
-  __shared__ double part[9][1024];
-  const int t = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int a = std::min(n, t * per), b = std::min(n, a + per);
-  double s[9];
-  for (int k = 0; k < 9; ++k) s[k] = 0.0;
-  for (int i = a; i < b; ++i)
-    for (int k = 0; k < 9; ++k) s[k] += vpart[9 * (size_t)i + k];
-  for (int k = 0; k < 9; ++k) part[k][t] = s[k];
-  __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (t < o)
-      for (int k = 0; k < 9; ++k) part[k][t] += part[k][t + o];
-    __syncthreads();
+// Forces of every atom.  The per-atom energies are complete before this
+// kernel starts, so when `energy` is given one extra workgroup (the last) forms
+// their total alongside the scatter and the call needs no reduction launch for
+// it; the virial total needs the whole scatter and runs after it (k_totals).
+template <bool VIRIAL>
+__global__ void __launch_bounds__(TT) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
+                                                const int32_t* __restrict__ col,
+                                                const int8_t* __restrict__ shift,
+                                                const int32_t* __restrict__ rev,
+                                                const double* __restrict__ pos, double Lx, double Ly,
+                                                double Lz, const float* __restrict__ g,
+                                                float* __restrict__ F, double* __restrict__ vpart,
+                                                const float* __restrict__ ei, float* __restrict__ energy) {
+  const int nblk = gridDim.x - (energy != nullptr ? 1 : 0);
+  if ((int)blockIdx.x == nblk) {
+    block_totals<false>(n, ei, nullptr, energy, nullptr);
+    return;
   }
-  if (t < 9) virial[t] = (float)part[t][0];
+  const int lane = threadIdx.x & 63;
+  for (int i = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TT) >> 6)
+    scatter_atom<VIRIAL>(i, lane, n, E, rp, col, shift, rev, pos, Lx, Ly, Lz, g, F, vpart);
 }
 
 // ------------------------------------------------------------ materialised basis
@@ -439,7 +464,6 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   p.off_g = o;     o += align256(4 * 3 * (size_t)E);
   p.off_ei = o;    o += align256(4 * (size_t)N);
   p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
-  p.off_epart = o; o += 256;
   p.off_w3t = o;   o += align256(4 * (size_t)p.P * 64 * p.NC);
   p.bytes = o;
   return p;
@@ -479,36 +503,32 @@ void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
     k_message<128><<<grid, 256, 0, s>>>(e0, e1, g->row_ptr, recv, R_chunk, Y_chunk, A);
 }
 
-void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts,
-                    float* ei, float* energy) {
-  if (p.N > 0) {
-    if (p.C == 64)
-      k_readout<64><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
-    else
-      k_readout<128><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
-  }
-  k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
-}
-
-void launch_energy_total(hipStream_t s, const ConvPlan& p, const float* ei, float* energy) {
-  k_energy_total<<<1, 1024, 0, s>>>(p.N, ei, energy);
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts, float* ei) {
+  if (p.N == 0) return;
+  if (p.C == 64)
+    k_readout<64><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
+  else
+    k_readout<128><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, nparts, m->w_read, A, ei);
 }
 
 void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
-                    const float* gin, float* forces, double* vpart, float* virial) {
+                    const float* gin, float* forces, const float* ei, float* energy, float* virial, char* ws) {
+  double* vpart = (double*)(ws + p.off_vpart);
   if (p.N == 0) {
-    if (virial) k_virial_total<<<1, 1024, 0, s>>>(0, vpart, virial);
+    if (virial)
+      k_totals<true><<<1, TT, 0, s>>>(0, ei, vpart, energy, virial);
+    else
+      k_totals<false><<<1, TT, 0, s>>>(0, ei, vpart, energy, virial);
     return;
   }
+  const int grid = blocks_for(p.N, TT / 64);
   if (virial) {
-    k_scatter<true><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev,
-                                                        pos, box.L[0], box.L[1], box.L[2], gin,
-                                                        forces, vpart);
-    k_virial_total<<<1, 1024, 0, s>>>(p.N, vpart, virial);
+    k_scatter<true><<<grid, TT, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0], box.L[1],
+                                         box.L[2], gin, forces, vpart, ei, nullptr);
+    k_totals<true><<<1, TT, 0, s>>>(p.N, ei, vpart, energy, virial);
   } else {
-    k_scatter<false><<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift,
-                                                         g->rev, pos, box.L[0], box.L[1], box.L[2],
-                                                         gin, forces, nullptr);
+    k_scatter<false><<<grid + 1, TT, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0],
+                                              box.L[1], box.L[2], gin, forces, vpart, ei, energy);
   }
 }
 

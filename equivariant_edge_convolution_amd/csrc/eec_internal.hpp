@@ -44,7 +44,7 @@ struct ConvPlan {
   int64_t chunk;  // edges per streamed chunk
   size_t bytes;
   size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_seg, off_A, off_R, off_Y, off_g,
-      off_epart, off_vpart, off_ei, off_w3t;
+      off_vpart, off_ei, off_w3t;
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
@@ -67,9 +67,8 @@ void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
                     const float* Y_chunk, float* A, const char* ws);
 
 // Readout: A_i = sum of `nparts` partial slabs [nparts][N][16][C] (fixed order),
-// E_i (into ei), the total energy, and dE/dA = 2 w A written over slab 0.
-void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts,
-                    float* ei, float* energy);
+// E_i (into ei) and dE/dA = 2 w A written over slab 0.
+void launch_readout(hipStream_t s, const ConvPlan& p, const eec_model* m, float* A, int nparts, float* ei);
 
 // Fused forward (C = 64): radial network + message per (pair, receiver) unit,
 // writing the S partial A slabs.  The chunked path (launch_radial +
@@ -84,9 +83,10 @@ void launch_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const
                      Box box, double cutoff, const int32_t* species, const eec_model* m,
                      const float* Abar, float* gout, const char* ws);
 
-// Force scatter (and optional virial).
-void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
-                    Box box, const float* gin, float* forces, double* vpart, float* virial);
+// Force scatter (and optional virial), the energy total from ei (and the
+// virial total).
+void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                    const float* gin, float* forces, const float* ei, float* energy, float* virial, char* ws);
 
 // Materialised basis / harmonics.
 void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box, double cutoff,
@@ -105,15 +105,14 @@ void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, 
 void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);
 
 // One species: the whole folded call per receiver in one kernel (forward tiles,
-// A_i, E_i into ei, dE/dA_i, backward tiles into gout).  Reads the transposed
-// last-layer weights launch_transpose_w3 wrote.
+// A_i, E_i into ei, dE/dA_i, backward tiles into gout).  When
+// fold_fused_needs_w3t, reads the transposed last-layer weights
+// launch_transpose_w3 wrote.
 bool fold_fused_supported(const ConvPlan& p);
+bool fold_fused_needs_w3t(const ConvPlan& p);
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
                        char* ws);
-
-// E = sum_i ei[i] (binary64, fixed order).
-void launch_energy_total(hipStream_t s, const ConvPlan& p, const float* ei, float* energy);
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

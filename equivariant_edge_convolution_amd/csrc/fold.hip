@@ -101,8 +101,9 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
 }
 
 // T of the unit to LDS, then acc[q][lm] = sum_k T[k][lm] W3[k][l(lm) C + c]
-// for channel c = lane + 64 q (the h_c factor is the caller's).
-template <int C>
+// for channel c = lane + 64 q (the h_c factor is the caller's).  W3[k][j] is
+// w3[k * SK + j] (global memory: SK = 4 C; LDS: its padded row stride).
+template <int C, int SK>
 __device__ __forceinline__ void unit_last_layer(const f32x16 T[2], float (*tsm)[NLM], const float* w3,
                                                 int lane, int s, int h, float acc[C / 64][NLM]) {
   constexpr int NC = 4 * C, CPL = C / 64;
@@ -128,7 +129,7 @@ __device__ __forceinline__ void unit_last_layer(const f32x16 T[2], float (*tsm)[
     }
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      const float* wr = w3 + (size_t)k * NC + lane + 64 * q;
+      const float* wr = w3 + (size_t)k * SK + lane + 64 * q;
       const float w0 = wr[0], wl1 = wr[C], wl2 = wr[2 * C], wl3 = wr[3 * C];
       acc[q][0] += t[0] * w0;
 #pragma unroll
@@ -175,7 +176,7 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
     T[1] = zero16();
     for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, un.perm, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
     float acc[CPL][NLM];
-    unit_last_layer<C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, s, h, acc);
+    unit_last_layer<C, 4 * C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, s, h, acc);
     float* ao = A_out + ((size_t)zs * N + i) * NLM * C;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -189,8 +190,10 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
 
 // ------------------------------------------------------------------ backward
 // M[lm][k] = sum_c (dE/dA h)[lm][c] W3[k][l(lm) C + c] from the staged ahsm rows
-// (lane = hidden k; wt = W3T of the pair + lane), into msm over the ahsm region.
-template <int C>
+// (lane = hidden k), into msm over the ahsm region.  W3[k][j] of this lane's k
+// is wt[j * SJ] (the transposed copy in global memory: SJ = 64; the LDS copy:
+// wt = its row k, SJ = 1).
+template <int C, int SJ>
 __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int lane, float (*msm)[HID + 1]) {
   float macc[NLM];
 #pragma unroll
@@ -203,8 +206,8 @@ __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int 
       const float4 x = *reinterpret_cast<const float4*>(&ahsm[c][4 * v]);
       av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
     }
-    const float w0 = wt[(size_t)c * HID], wl1 = wt[(size_t)(C + c) * HID];
-    const float wl2 = wt[(size_t)(2 * C + c) * HID], wl3 = wt[(size_t)(3 * C + c) * HID];
+    const float w0 = wt[(size_t)c * SJ], wl1 = wt[(size_t)(C + c) * SJ];
+    const float wl2 = wt[(size_t)(2 * C + c) * SJ], wl3 = wt[(size_t)(3 * C + c) * SJ];
     macc[0] += av[0] * w0;
 #pragma unroll
     for (int lm = 1; lm < 4; ++lm) macc[lm] += av[lm] * wl1;
@@ -362,7 +365,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
       for (int lm = 0; lm < NLM; ++lm) L.ahsm[c][lm] = ar[lm * C] * hc;
     }
     wave_sync_lds();
-    unit_M<C>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
+    unit_M<C, HID>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
     for (int q0 = qa; q0 < qb; q0 += 32)
       bwd_tile(in, un.perm, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
   }
@@ -375,22 +378,27 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
 // tiles, so A never leaves the chip and the readout needs no kernel of its own.
 // (The forward's activations are recomputed in the backward tiles: keeping them
 // would cost a round trip of 3 x 64 floats per edge through HBM, more than the
-// two layers take to redo.)
-template <int C, int W>
+// two layers take to redo.)  With W3L the last layer's weights sit in LDS too
+// (C = 64: 64 KB), read along rows for A and down columns for M, so neither
+// needs the transposed copy and the units of a workgroup share one read of W3.
+template <int C, int W, bool W3L>
 __global__ void __launch_bounds__(64 * W)
 k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
              const float* __restrict__ W3, const float* __restrict__ W3T, const float* __restrict__ emb,
              const float* __restrict__ w_read, float* __restrict__ ei, float* __restrict__ gout) {
   constexpr int CPL = C / 64;
-  __shared__ float w12[W12_FLOATS];
+  __shared__ float wl[W3L ? Lds<C>::FLOATS : W12_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
-  const float* w1s = w12;
-  const float* w2s = w12 + NB * LDH;
+  const float* w1s = wl + Lds<C>::W1;
+  const float* w2s = wl + Lds<C>::W2;
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  stage_w12(w12, W1, W2, 0);
+  if (W3L)
+    stage_weights<C>(wl, W1, W2, W3, 0);
+  else
+    stage_w12(wl, W1, W2, 0);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
@@ -403,7 +411,10 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     T[1] = zero16();
     for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, nullptr, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
     float acc[CPL][NLM];
-    unit_last_layer<C>(T, L.tsm, W3, lane, s, h, acc);
+    if (W3L)
+      unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, s, h, acc);
+    else
+      unit_last_layer<C, 4 * C>(T, L.tsm, W3, lane, s, h, acc);
     // E_i = sum_c w_c sum_lm A^2 and dE/dA h = 2 w_c A h_c, A = h_c acc
     float esum = 0.f;
 #pragma unroll
@@ -423,7 +434,10 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     if (lane == 0) ei[i] = esum;
     if (qb <= qa) continue;
     wave_sync_lds();
-    unit_M<C>(L.ahsm, W3T + lane, lane, L.msm);
+    if (W3L)
+      unit_M<C, 1>(L.ahsm, wl + Lds<C>::W3 + lane * Lds<C>::LD3, lane, L.msm);
+    else
+      unit_M<C, HID>(L.ahsm, W3T + lane, lane, L.msm);
     for (int q0 = qa; q0 < qb; q0 += 32)
       bwd_tile(in, nullptr, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
   }
@@ -495,6 +509,7 @@ void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, c
 }
 
 bool fold_fused_supported(const ConvPlan& p) { return p.S == 1; }
+bool fold_fused_needs_w3t(const ConvPlan& p) { return p.C != 64; }
 
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
@@ -504,9 +519,11 @@ void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
   if (p.C == 64)
-    k_fold_fused<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ei, gout);
+    k_fold_fused<64, WAVES, true><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, nullptr, m->emb,
+                                                                       m->w_read, ei, gout);
   else
-    k_fold_fused<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ei, gout);
+    k_fold_fused<128, WAVES, false><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb,
+                                                                         m->w_read, ei, gout);
 }
 
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

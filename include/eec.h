@@ -227,17 +227,18 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * (created by the caller, e.g. with hipEventCreate) recorded on `stream` around
  * each phase: events[2k] before and events[2k+1] after phase k, for
  *   k = EEC_PHASE_PREPARE   receiver index and pair grouping (folded, one
- *                           species: the transpose of W3 only),
+ *                           species: the transpose of W3 for C != 64 only),
  *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
  *                           radial-row chunks and message passes; folded,
  *                           one species: the single fused kernel launch,
  *                           forward and backward),
- *       EEC_PHASE_READOUT   per-atom energies, dE/dA, total energy (folded,
- *                           one species: the total energy only),
+ *       EEC_PHASE_READOUT   per-atom energies and dE/dA (folded, one
+ *                           species: empty),
  *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch; the
  *                           folded variant also transposes W3 first; folded,
  *                           one species: empty),
- *       EEC_PHASE_SCATTER   forces (and virial).
+ *       EEC_PHASE_SCATTER   forces and the energy total in one kernel launch
+ *                           (with the virial, a second launch totals both).
  * `events` holds 2 * EEC_N_PHASES handles; NULL records nothing.  Results are
  * bit for bit those of the untimed call. */
 enum { EEC_PHASE_PREPARE = 0, EEC_PHASE_FORWARD = 1, EEC_PHASE_READOUT = 2,
