@@ -148,6 +148,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-variant", action="store_true",
+                    help="time only --variant (for profiler runs that should see one kernel family)")
     ap.add_argument("--variant", default="folded", choices=["direct", "folded"],
                     help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
                          "last radial layer moved past the edge sum (eec_energy_forces_folded)")
@@ -206,7 +208,8 @@ def main() -> int:
 
     ms_per_step, phase_ms, energy = timed(args.variant, args.steps, args.warmup)
     other = "direct" if args.variant == "folded" else "folded"
-    o_ms, o_phase, o_energy = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+    if not args.no_other_variant:
+        o_ms, o_phase, o_energy = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
     # units with at least one edge: (receiver, sender species) pairs present in the graph
     rp = g.row_ptr.cpu().numpy()
@@ -243,10 +246,10 @@ def main() -> int:
                      "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
                      "flop_per_launch": flop, "launch_ms": launch_ms},
         "variant": args.variant,
-        "variants": {other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase,
-                             "energy": o_energy,
-                             "roofline_kernel": roof(other, o_phase)[0],
-                             "roofline_frac": roof(other, o_phase)[3] / PEAK_FP32_MFMA_TFLOPS}},
+        "variants": {} if args.no_other_variant else {
+            other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase, "energy": o_energy,
+                    "roofline_kernel": roof(other, o_phase)[0],
+                    "roofline_frac": roof(other, o_phase)[3] / PEAK_FP32_MFMA_TFLOPS}},
         "phases_ms": phase_ms,
         "neighbors_ms": nb_ms,
         "energy": energy,

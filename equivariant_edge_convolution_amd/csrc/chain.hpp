@@ -134,7 +134,9 @@ __device__ __forceinline__ void layer2(const float* __restrict__ w2s, const f32x
   }
 }
 
-// s = silu(z) and d = silu'(z) from one sigmoid evaluation.
+// s = silu(z) and d = silu'(z) from one sigmoid evaluation.  d is pinned to
+// registers here: left to itself the compiler sinks it to its late use and
+// keeps both z and the sigmoid live instead, twice the registers.
 __device__ __forceinline__ void silu_and_deriv(const f32x16 z[2], f32x16 s[2], f32x16 d[2]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -142,7 +144,9 @@ __device__ __forceinline__ void silu_and_deriv(const f32x16 z[2], f32x16 s[2], f
     for (int r = 0; r < 16; ++r) {
       const float zz = z[m][r], sg = sigmoid(zz);
       s[m][r] = zz * sg;
-      d[m][r] = sg * (1.f + zz * (1.f - sg));
+      float dd = sg * (1.f + zz * (1.f - sg));
+      asm volatile("" : "+v"(dd));
+      d[m][r] = dd;
     }
 }
 
