@@ -104,6 +104,22 @@ __device__ __forceinline__ void stage_weights(float* lds, const float* __restric
     lds[Lds<C>::W3 + (k / NC) * Lds<C>::LD3 + k % NC] = w3[k];
 }
 
+// Schedule of a run of NMFMA matrix instructions whose B operands come from
+// LDS (one read per PER instructions): PRE reads are issued ahead and each group
+// of PER instructions is followed by the next read, so PRE reads stay in flight.
+// Left alone the scheduler issues each read just before its use and waits on
+// it, which stalls the matrix pipe for the LDS latency every PER instructions.
+template <int NMFMA, int PER, int PRE>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+  for (int k = 0; k < NMFMA / PER - PRE; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PER * PRE, 0);
+}
+
 // Input hidden feature of K-step ks (0..31) carried by a lane of half h when the
 // 64 hidden features sit in two edges-on-N accumulator tiles: hid_k0(ks) + 4 h.
 __device__ __forceinline__ constexpr int hid_k0(int ks) { return 32 * (ks >> 4) + fperm(ks & 15); }
@@ -118,6 +134,7 @@ __device__ __forceinline__ void layer1(const float* __restrict__ w1s, const floa
   for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
     for (int m = 0; m < 2; ++m) z[m] = mfma32(w[ks * LDH + 32 * m], b[ks], z[m]);
+  pipeline_lds_mfma<32, 2, 6>();
 }
 
 // z2 = s1 W2 (edges on N).
@@ -132,6 +149,7 @@ __device__ __forceinline__ void layer2(const float* __restrict__ w2s, const f32x
 #pragma unroll
     for (int m = 0; m < 2; ++m) z[m] = mfma32(w[hid_k0(ks) * LDH + 32 * m], bv, z[m]);
   }
+  pipeline_lds_mfma<64, 2, 6>();
 }
 
 // s = silu(z) and d = silu'(z) from one sigmoid evaluation.  d is pinned to
@@ -186,6 +204,47 @@ __device__ __forceinline__ Geo edge_geo_at(const EdgeIn& in, int64_t e, int i) {
 }
 
 __device__ __forceinline__ Geo edge_geo(const EdgeIn& in, int64_t e) { return edge_geo_at(in, e, in.recv[e]); }
+
+// The global loads behind an edge's geometry (sender position and image shift).
+struct EdgeRaw {
+  double xj, yj, zj;
+  int sx, sy, sz;
+};
+
+__device__ __forceinline__ EdgeRaw edge_raw(const EdgeIn& in, int64_t e) {
+  EdgeRaw w;
+  const int j = min(max(in.col[e], 0), in.n_atoms - 1);
+  w.xj = in.pos[3 * j + 0];
+  w.yj = in.pos[3 * j + 1];
+  w.zj = in.pos[3 * j + 2];
+  const int8_t* sh = in.shift + 3 * e;
+  w.sx = sh[0];
+  w.sy = sh[1];
+  w.sz = sh[2];
+  return w;
+}
+
+// edge_geo_at from prefetched loads and the receiver's position xi: the same
+// binary64 operations in the same order as edge_vector.
+__device__ __forceinline__ Geo geo_from_raw(const EdgeIn& in, const EdgeRaw& w, const double xi[3]) {
+#pragma clang fp contract(off)
+  double d[3];
+  d[0] = (w.xj - xi[0]) + (double)w.sx * in.Lx;
+  d[1] = (w.yj - xi[1]) + (double)w.sy * in.Ly;
+  d[2] = (w.zj - xi[2]) + (double)w.sz * in.Lz;
+  const double r2 = norm2_nofma(d);
+  const double r = sqrt(r2);
+  const double ir = 1.0 / r;
+  Geo g;
+  g.r = r;
+  g.inv_r = (float)ir;
+  g.ux = (float)(d[0] * ir);
+  g.uy = (float)(d[1] * ir);
+  g.uz = (float)(d[2] * ir);
+  g.i = -1;
+  g.j = -1;
+  return g;
+}
 
 
 // Work units of the receiver-aligned kernels: (ordered species pair p, receiver i).

@@ -465,6 +465,7 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   p.off_ei = o;    o += align256(4 * (size_t)N);
   p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
   p.off_w3t = o;   o += align256(4 * (size_t)p.P * 64 * p.NC);
+  p.off_stash = o; o += align256(fold_stash_bytes(p));
   p.bytes = o;
   return p;
 }

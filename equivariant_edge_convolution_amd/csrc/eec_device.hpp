@@ -90,13 +90,15 @@ __device__ __forceinline__ double envelope_d(double x) {
 // (16 theta) and one rotation by theta, which costs a few ulps of binary64.
 struct BasisStart {
   double s, c;    // sin, cos of n0 theta
-  double s1, c1;  // sin, cos of theta
+  double sp, cp;  // sin, cos of (n0 - 1) theta
+  double c1;      // cos theta
 };
 
 __device__ __forceinline__ BasisStart basis_start(double r, double rc, int h) {
   BasisStart b;
-  sincos(PI / rc * r, &b.s1, &b.c1);
-  double s = b.s1, c = b.c1;
+  double s1, c1;
+  sincos(PI / rc * r, &s1, &c1);
+  double s = s1, c = c1;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {  // 2^4 theta
     const double s2 = 2.0 * s * c;
@@ -104,38 +106,43 @@ __device__ __forceinline__ BasisStart basis_start(double r, double rc, int h) {
     s = s2;
     c = c2;
   }
-  const double s17 = s * b.c1 + c * b.s1, c17 = c * b.c1 - s * b.s1;
-  b.s = h ? s17 : b.s1;
-  b.c = h ? c17 : b.c1;
+  const double s17 = s * c1 + c * s1, c17 = c * c1 - s * s1;
+  b.s = h ? s17 : s1;
+  b.c = h ? c17 : c1;
+  b.sp = h ? s : 0.0;
+  b.cp = h ? c : 1.0;
+  b.c1 = c1;
   return b;
 }
 
-// Basis functions n = n0 .. n0 + 15 of b_n = sin(n pi r / rc) / r * env(r / rc),
-// by the angle-addition recurrence in binary64 from a BasisStart; optionally
-// db_n / dr.
+// Basis functions n = n0 .. n0 + 15 of b_n = sin(n pi r / rc) / r * env(r / rc)
+// by the three-term recurrence sin((n+1)t) = 2 cos t sin(nt) - sin((n-1)t) (and
+// the same for cos) in binary64 from a BasisStart; optionally db_n / dr.
 template <bool DERIV>
 __device__ __forceinline__ void basis16_from(const BasisStart& st, double r, double rc, int n0,
                                              float b[16], float db[16]) {
-  double s = st.s, c = st.c;
-  const double s1 = st.s1, c1 = st.c1;
+  double s = st.s, sp = st.sp, c = st.c, cp = st.cp;
+  const double two_c1 = 2.0 * st.c1;
   const double x = r / rc;
   const double env = envelope(x);
   const double inv_r = 1.0 / r;
-  const double envd = DERIV ? envelope_d(x) / rc : 0.0;
-  const double kstep = PI / rc;
-  double kn = (double)n0 * kstep;  // n pi / rc, advanced with n
+  const double A = inv_r * env;                                        // b_n = s_n A
+  const double Bd = DERIV ? inv_r * (envelope_d(x) / rc - A) : 0.0;   // db_n = c_n n k A + s_n Bd
+  const double kA0 = PI / rc * A;
+  double kA = (double)n0 * kA0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const double sr = s * inv_r;
-    b[k] = (float)(sr * env);
+    b[k] = (float)(s * A);
     if (DERIV) {
-      db[k] = (float)((kn * c * inv_r - sr * inv_r) * env + sr * envd);
-      kn += kstep;
+      db[k] = (float)(c * kA + s * Bd);
+      kA += kA0;
+      const double cn = two_c1 * c - cp;
+      cp = c;
+      c = cn;
     }
-    const double sn = s * c1 + c * s1;
-    const double cn = c * c1 - s * s1;
+    const double sn = two_c1 * s - sp;
+    sp = s;
     s = sn;
-    c = cn;
   }
 }
 

@@ -44,7 +44,7 @@ struct ConvPlan {
   int64_t chunk;  // edges per streamed chunk
   size_t bytes;
   size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_seg, off_A, off_R, off_Y, off_g,
-      off_vpart, off_ei, off_w3t;
+      off_vpart, off_ei, off_w3t, off_stash;
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
@@ -100,6 +100,10 @@ void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, c
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                           Box box, double cutoff, const int32_t* species, const eec_model* m,
                           const float* Abar, float* gout, char* ws);
+
+// Bytes of the per-wave activation stash of the one-species fused kernel
+// (bounded by its grid, not by the edge count; 0 for several species).
+size_t fold_stash_bytes(const ConvPlan& p);
 
 // W3T[p][j][k] = W3[p][k][j] into the workspace (read by the folded backward).
 void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);

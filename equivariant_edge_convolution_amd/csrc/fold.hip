@@ -52,24 +52,83 @@ struct WaveLds {
   }
 };
 
-// ------------------------------------------------------------------ forward
-// One 32-edge tile [q0, q0 + 32) of unit (p, i) (positions in the work order,
-// `perm` maps them to CSR edges; NULL = identity): T += s2^T Y over the tile.
-__device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const float* w1s,
-                                         const float* w2s, float (*ysm)[NLM + 1], int i, int q0,
-                                         int qa, int qb, int s, int h, f32x16 T[2]) {
+// ------------------------------------------------------------------ stash
+// One-species fused kernel: what the backward tiles of a unit need from its
+// forward tiles, kept in a per-wave scratch region instead of recomputing the
+// radial basis and the first two layers.  Row of an edge (ZROW floats):
+//   [0, 64)    silu'(z1) by hidden index
+//   [64, 128)  z2 by hidden index
+//   [128, 136) u_x, u_y, u_z, 1/r (float32), r (binary64 as two words), 2 spare
+// A unit's first STASH_TILES tiles are kept; further tiles (rows denser than
+// STASH_TILES * 32 edges) recompute.  The live rows of all waves (about 85 MB
+// for a 4096-atom diamond) stay in the last-level cache between the forward
+// and the backward of a unit, where re-reading them is cheaper than the two
+// layers it saves.
+constexpr int ZROW = 2 * HID + 8;
+constexpr int STASH_TILES = 6;
+
+// ------------------------------------------------------------------ tiles
+// Edge of lane slot s in the tile starting at position q0 of a unit whose edges
+// sit at positions [qa, qb) of the work order (`perm` maps positions to CSR
+// edges; NULL = identity).  Padding slots repeat the unit's first edge.
+__device__ __forceinline__ int64_t tile_edge(const int32_t* perm, int q0, int qa, int qb, int s) {
   const int q = q0 + s;
-  const bool valid = q < qb;
-  const int qq = valid ? q : qa;
-  const int64_t e = perm ? (int64_t)perm[qq] : (int64_t)qq;
-  const Geo g = edge_geo_at(in, e, i);
+  const int qq = q < qb ? q : qa;
+  return perm ? (int64_t)perm[qq] : (int64_t)qq;
+}
+
+// Receiver position of unit atom i.
+struct Recv {
+  double x[3];
+};
+__device__ __forceinline__ Recv recv_pos(const EdgeIn& in, int i) {
+  i = min(max(i, 0), in.n_atoms - 1);
+  return Recv{{in.pos[3 * i], in.pos[3 * i + 1], in.pos[3 * i + 2]}};
+}
+
+// Stash rows of the tile at position q0 of a unit starting at qa, in the
+// region `zw` of the wave; NULL when the tile is past the kept ones.
+__device__ __forceinline__ float* stash_tile(float* zw, int q0, int qa) {
+  const int t = (q0 - qa) >> 5;
+  return zw != nullptr && t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr;
+}
+
+// ------------------------------------------------------------------ forward
+// One 32-edge tile [q0, q0 + 32) of a unit: T += s2^T Y over the tile.  With a
+// stash tile zs, also its rows (edge slot k at zs + k ZROW).
+__device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const Recv& xi,
+                                         const float* w1s, const float* w2s, float (*ysm)[NLM + 1],
+                                         int q0, int qa, int qb, int s, int h, f32x16 T[2], float* zs) {
+  const bool valid = q0 + s < qb;
+  const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
+  if (zs != nullptr && valid && h == 0) {
+    float* row = zs + s * ZROW + 2 * HID;
+    float rw[2];
+    __builtin_memcpy(rw, &g.r, sizeof(double));
+    *reinterpret_cast<float4*>(row) = make_float4(g.ux, g.uy, g.uz, g.inv_r);
+    *reinterpret_cast<float2*>(row + 4) = make_float2(rw[0], rw[1]);
+  }
   f32x16 z[2], a[2];
   {
     float bas[16];
     basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
     layer1(w1s, bas, s, h, z);
   }
-  silu_tiles(z, a);  // s1, edges on N
+  if (zs != nullptr) {
+    f32x16 d[2];
+    silu_and_deriv(z, a, d);  // s1 and silu'(z1), edges on N: hidden hid_k0(ks) + 4h
+    if (valid) {
+      float* row = zs + s * ZROW + 4 * h;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(row + 32 * m + 8 * j) =
+              make_float4(d[m][4 * j], d[m][4 * j + 1], d[m][4 * j + 2], d[m][4 * j + 3]);
+    }
+  } else {
+    silu_tiles(z, a);  // s1, edges on N
+  }
   // z2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s
   {
     const float* w = w2s + 4 * h * LDH + s;  // W2[hid_k0(ks) + 4 h][32 m + s]
@@ -81,13 +140,26 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
 #pragma unroll
       for (int m = 0; m < 2; ++m) z[m] = mfma32(av, w[hid_k0(ks) * LDH + 32 * m], z[m]);
     }
+    pipeline_lds_mfma<64, 2, 6>();
+  }
+  if (zs != nullptr) {
+    // z2 rows: register r of tile m is edge slot fperm(r) + 4h, hidden 32 m + s
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = fperm(r) + 4 * h;
+      if (q0 + k < qb) {
+        float* row = zs + k * ZROW + HID + s;
+        row[0] = z[0][r];
+        row[32] = z[1][r];
+      }
+    }
   }
   silu_tiles(z, a);  // s2, edges on M
   {
     float Y[16];
     sph16(g.ux, g.uy, g.uz, Y);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ysm[s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
+    for (int k = 0; k < 8; ++k) ysm[s][8 * h + k] = valid ? (h ? Y[8 + k] : Y[k]) : 0.f;  // static indices
   }
   wave_sync_lds();
   // T[hidden][lm] += sum over this tile's edges (K = edges, pairs (fperm(ks), fperm(ks)+4))
@@ -97,6 +169,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
 #pragma unroll
     for (int m = 0; m < 2; ++m) T[m] = mfma32(a[m][ks], yv, T[m]);
   }
+  pipeline_lds_mfma<32, 2, 6>();
   wave_sync_lds();
 }
 
@@ -174,7 +247,9 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
     f32x16 T[2];
     T[0] = zero16();
     T[1] = zero16();
-    for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, un.perm, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
+    const Recv xi = recv_pos(in, i);
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, nullptr);
     float acc[CPL][NLM];
     unit_last_layer<C, 4 * C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, s, h, acc);
     float* ao = A_out + ((size_t)zs * N + i) * NLM * C;
@@ -222,18 +297,39 @@ __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int 
   wave_sync_lds();
 }
 
-// One 32-edge tile of the backward of unit (p, i): g = dE/dd of its edges.
-__device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, const float* w1s,
-                                         const float* w2s, float (*msm)[HID + 1], float (*ybsm)[NLM + 1],
-                                         int i, int q0, int qa, int qb, int s, int h,
-                                         float* __restrict__ gout) {
-  const int q = q0 + s;
-  const bool valid = q < qb;
-  const int qq = valid ? q : qa;
-  const int64_t e = perm ? (int64_t)perm[qq] : (int64_t)qq;
-  const Geo g = edge_geo_at(in, e, i);
+// One 32-edge tile of the backward of a unit: g = dE/dd of its edges.  The
+// geometry, silu'(z1) and z2 come from the stash tile zs when given, else are
+// recomputed.
+__device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const int32_t* perm,
+                                         const float* w1s, const float* w2s, float (*msm)[HID + 1],
+                                         float (*ybsm)[NLM + 1], int q0, int qa, int qb, int s, int h,
+                                         float* __restrict__ gout, const float* zs) {
+  const bool valid = q0 + s < qb;
+  const int64_t e = tile_edge(perm, q0, qa, qb, s);
+  Geo g;
   f32x16 d1[2], d2[2], s2[2];  // silu'(z1), silu'(z2), silu(z2); edges on N
-  {
+  if (zs != nullptr) {
+    const float* row = zs + (valid ? s : 0) * ZROW;
+    const float4 u = *reinterpret_cast<const float4*>(row + 2 * HID);
+    const float2 rw = *reinterpret_cast<const float2*>(row + 2 * HID + 4);
+    g.ux = u.x;
+    g.uy = u.y;
+    g.uz = u.z;
+    g.inv_r = u.w;
+    __builtin_memcpy(&g.r, &rw, sizeof(double));
+    f32x16 z[2], s1[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v1 = *reinterpret_cast<const float4*>(row + 4 * h + 32 * m + 8 * j);
+        const float4 v2 = *reinterpret_cast<const float4*>(row + HID + 4 * h + 32 * m + 8 * j);
+        d1[m][4 * j] = v1.x; d1[m][4 * j + 1] = v1.y; d1[m][4 * j + 2] = v1.z; d1[m][4 * j + 3] = v1.w;
+        z[m][4 * j] = v2.x; z[m][4 * j + 1] = v2.y; z[m][4 * j + 2] = v2.z; z[m][4 * j + 3] = v2.w;
+      }
+    silu_and_deriv(z, s2, d2);
+  } else {
+    g = geo_from_raw(in, edge_raw(in, e), xi.x);
     f32x16 z[2], s1[2];
     {
       float bas[16];
@@ -254,6 +350,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, 
       const float bv = s < NLM ? mr[hid_k0(ks)] : 0.f;
       yb = mfma32(s2[ks >> 4][ks & 15], bv, yb);
     }
+    pipeline_lds_mfma<32, 2, 6>();
   }
   __builtin_amdgcn_sched_barrier(0);
   // s2bar[k][edge] = sum_lm M[lm][k] Y[edge][lm]  (edges on N; K pairs (2ks, 2ks + 1))
@@ -270,6 +367,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, 
 #pragma unroll
       for (int m = 0; m < 2; ++m) sb[m] = mfma32(mc[2 * ks * (HID + 1) + 32 * m], bv, sb[m]);
     }
+    pipeline_lds_mfma<16, 2, 6>();
   }
   __builtin_amdgcn_sched_barrier(0);
   // Ybar to the lanes that own the edges, contracted with the harmonic gradients
@@ -300,6 +398,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, 
 #pragma unroll
     for (int m = 0; m < 2; ++m) s1b[m] = mfma32(w2c[32 * m * LDH + hid_k0(ks)], bv, s1b[m]);
   }
+  pipeline_lds_mfma<64, 2, 6>();
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -308,6 +407,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const int32_t* perm, 
   const float* w1c = w1s + basis_of_row(s) * LDH + 4 * h;
 #pragma unroll
   for (int ks = 0; ks < 32; ++ks) bb = mfma32(w1c[hid_k0(ks)], s1b[ks >> 4][ks & 15], bb);
+  pipeline_lds_mfma<32, 2, 6>();
   __builtin_amdgcn_sched_barrier(0);
   float rbar = 0.f;
   {
@@ -366,8 +466,9 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
     }
     wave_sync_lds();
     unit_M<C, HID>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
+    const Recv xi = recv_pos(in, i);
     for (int q0 = qa; q0 < qb; q0 += 32)
-      bwd_tile(in, un.perm, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
+      bwd_tile(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, nullptr);
   }
 }
 
@@ -385,7 +486,8 @@ template <int C, int W, bool W3L>
 __global__ void __launch_bounds__(64 * W)
 k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
              const float* __restrict__ W3, const float* __restrict__ W3T, const float* __restrict__ emb,
-             const float* __restrict__ w_read, float* __restrict__ ei, float* __restrict__ gout) {
+             const float* __restrict__ w_read, float* __restrict__ ei, float* __restrict__ gout,
+             float* __restrict__ stash) {
   constexpr int CPL = C / 64;
   __shared__ float wl[W3L ? Lds<C>::FLOATS : W12_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
@@ -409,7 +511,10 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     f32x16 T[2];
     T[0] = zero16();
     T[1] = zero16();
-    for (int q0 = qa; q0 < qb; q0 += 32) fwd_tile(in, nullptr, w1s, w2s, L.ysm, i, q0, qa, qb, s, h, T);
+    const Recv xi = recv_pos(in, i);
+    float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
     float acc[CPL][NLM];
     if (W3L)
       unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, s, h, acc);
@@ -439,7 +544,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     else
       unit_M<C, HID>(L.ahsm, W3T + lane, lane, L.msm);
     for (int q0 = qa; q0 < qb; q0 += 32)
-      bwd_tile(in, nullptr, w1s, w2s, L.msm, L.ybsm, i, q0, qa, qb, s, h, gout);
+      bwd_tile(in, xi, nullptr, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
   }
 }
 
@@ -490,6 +595,11 @@ int unit_grid(const ConvPlan& p) {
 
 }  // namespace
 
+size_t fold_stash_bytes(const ConvPlan& p) {
+  if (p.S != 1) return 0;
+  return sizeof(float) * (size_t)unit_grid(p) * WAVES * STASH_TILES * 32 * ZROW;
+}
+
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                          Box box, double cutoff, const int32_t* species, const eec_model* m,
                          float* A_out, char* ws) {
@@ -516,14 +626,15 @@ void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
                        char* ws) {
   if (p.N == 0) return;
   const float* W3T = (const float*)(ws + p.off_w3t);
+  float* stash = (float*)(ws + p.off_stash);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
   if (p.C == 64)
     k_fold_fused<64, WAVES, true><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, nullptr, m->emb,
-                                                                       m->w_read, ei, gout);
+                                                                       m->w_read, ei, gout, stash);
   else
     k_fold_fused<128, WAVES, false><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb,
-                                                                         m->w_read, ei, gout);
+                                                                         m->w_read, ei, gout, stash);
 }
 
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

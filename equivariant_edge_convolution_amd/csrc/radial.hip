@@ -79,7 +79,7 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
       sph16(g.ux, g.uy, g.uz, Y);
       float* yo = Y_out + (e - row_base) * NLM + 8 * h;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) yo[k] = Y[8 * h + k];
+      for (int k = 0; k < 8; ++k) yo[k] = h ? Y[8 + k] : Y[k];
     }
     f32x16 z[2], a[2];
     layer1(w1s, bas, s, h, z);
@@ -187,7 +187,7 @@ k_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __rest
         float Y[16];
         sph16(g.ux, g.uy, g.uz, Y);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ysm[wave][s][8 * h + k] = valid ? Y[8 * h + k] : 0.f;
+        for (int k = 0; k < 8; ++k) ysm[wave][s][8 * h + k] = valid ? (h ? Y[8 + k] : Y[k]) : 0.f;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
