@@ -256,7 +256,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
                    model_span(m->w_read, m, 5)}));
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int k) {
-    if (events != nullptr) hipEventRecord((hipEvent_t)events[k], s);
+    if (events != nullptr && events[k] != nullptr) hipEventRecord((hipEvent_t)events[k], s);
   };
   char* ws = (char*)workspace;
   float* A = (float*)(ws + p.off_A);
@@ -285,6 +285,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   }
   mark(2 * EEC_PHASE_PREPARE);
   launch_prepare(s, p, g, species, ws, A);
+  if (folded) launch_transpose_w3(s, p, m, ws);
   mark(2 * EEC_PHASE_PREPARE + 1);
   mark(2 * EEC_PHASE_FORWARD);
   int nparts = 1;

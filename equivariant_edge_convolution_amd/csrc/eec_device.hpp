@@ -38,6 +38,28 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// 16x16x4 tiles: A lane l holds A[l % 16][l / 16], B lane l holds
+// B[l / 16][l % 16], accumulator register i of lane l holds D[4 (l / 16) + i][l % 16].
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Exchange 16-lane rows between two registers: on return `a` holds rows
+// (a0, b0, a2, b2) and `b` rows (a1, b1, a3, b3) of the inputs (row k = lanes
+// 16 k .. 16 k + 15).  Regroups a 32-wide tile layout into 16-wide ones.
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -93,7 +93,8 @@ void launch_basis(hipStream_t s, const eec_graph* g, const double* pos, Box box,
                   float* r, float* basis, float* Y);
 
 // Reassociated last layer (the fold): forward per unit into the S partial A
-// slabs; backward (also writes the transposed last-layer weights it reads).
+// slabs; backward (reads the transposed last-layer weights launch_transpose_w3
+// wrote).
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
                          Box box, double cutoff, const int32_t* species, const eec_model* m,
                          float* A_out, char* ws);

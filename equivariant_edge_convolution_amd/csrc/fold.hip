@@ -98,7 +98,7 @@ __device__ __forceinline__ float* stash_tile(float* zw, int q0, int qa) {
 // stash tile zs, also its rows (edge slot k at zs + k ZROW).
 __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const Recv& xi,
                                          const float* w1s, const float* w2s, float (*ysm)[NLM + 1],
-                                         int q0, int qa, int qb, int s, int h, f32x16 T[2], float* zs) {
+                                         int q0, int qa, int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
   if (zs != nullptr && valid && h == 0) {
@@ -162,14 +162,26 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
     for (int k = 0; k < 8; ++k) ysm[s][8 * h + k] = valid ? (h ? Y[8 + k] : Y[k]) : 0.f;  // static indices
   }
   wave_sync_lds();
-  // T[hidden][lm] += sum over this tile's edges (K = edges, pairs (fperm(ks), fperm(ks)+4))
+  // T[hidden][lm] += sum over this tile's edges on 16x16x4 tiles (N = the 16
+  // harmonics exactly).  Swapping rows of registers r and r + 4 of tile m
+  // leaves, in lane j + 16 q, hidden 32 m + j (register r) and 32 m + 16 + j
+  // (register r + 4) of edge fperm(r) + off(q), off = 0, 8, 4, 12: the A
+  // operands of hidden blocks 2m and 2m + 1 for K = those four edges.
+  {
+    const int j = s & 15, qk = (s >> 4) + 2 * h;
+    const float* yrow = &ysm[8 * (qk & 1) + 4 * (qk >> 1)][j];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const float yv = s < NLM ? ysm[fperm(ks) + 4 * h][s] : 0.f;
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) T[m] = mfma32(a[m][ks], yv, T[m]);
+      for (int rr = 0; rr < 12; rr = (rr == 3 ? 8 : rr + 1)) {
+        float lo = a[m][rr], hi = a[m][rr + 4];
+        swap_rows16(lo, hi);
+        const float yv = yrow[fperm(rr) * (NLM + 1)];
+        T[2 * m] = mfma16(lo, yv, T[2 * m]);
+        T[2 * m + 1] = mfma16(hi, yv, T[2 * m + 1]);
+      }
+    pipeline_lds_mfma<32, 2, 6>();
   }
-  pipeline_lds_mfma<32, 2, 6>();
   wave_sync_lds();
 }
 
@@ -177,16 +189,14 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
 // for channel c = lane + 64 q (the h_c factor is the caller's).  W3[k][j] is
 // w3[k * SK + j] (global memory: SK = 4 C; LDS: its padded row stride).
 template <int C, int SK>
-__device__ __forceinline__ void unit_last_layer(const f32x16 T[2], float (*tsm)[NLM], const float* w3,
-                                                int lane, int s, int h, float acc[C / 64][NLM]) {
-  constexpr int NC = 4 * C, CPL = C / 64;
-  // T register r of tile m, lane (s, h): hidden 32 m + fperm(r) + 4h, harmonic s (< 16)
-  if (s < NLM) {
+__device__ __forceinline__ void unit_last_layer(const f32x4 T[4], float (*tsm)[NLM], const float* w3,
+                                                int lane, float acc[C / 64][NLM]) {
+  constexpr int CPL = C / 64;
+  // T block b register i, lane l: hidden 16 b + 4 (l / 16) + i, harmonic l % 16
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tsm[32 * m + fperm(r) + 4 * h][s] = T[m][r];
-  }
+    for (int i = 0; i < 4; ++i) tsm[16 * b + 4 * (lane >> 4) + i][lane & 15] = T[b][i];
   wave_sync_lds();
 #pragma unroll
   for (int q = 0; q < CPL; ++q)
@@ -244,14 +254,14 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
     int s = lane & 31, h = lane >> 5;
     asm volatile("" : "+v"(s), "+v"(h));
     const int zs = p % S;
-    f32x16 T[2];
-    T[0] = zero16();
-    T[1] = zero16();
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
     const Recv xi = recv_pos(in, i);
     for (int q0 = qa; q0 < qb; q0 += 32)
       fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, nullptr);
     float acc[CPL][NLM];
-    unit_last_layer<C, 4 * C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, s, h, acc);
+    unit_last_layer<C, 4 * C>(T, L.tsm, W3 + (size_t)p * HID * 4 * C, lane, acc);
     float* ao = A_out + ((size_t)zs * N + i) * NLM * C;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -341,15 +351,26 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
     silu_and_deriv(z, s2, d2);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k]  (edges on M; lane column = lm)
-  f32x16 yb = zero16();
+  // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k] on 16x16x4 tiles: swapping rows
+  // of registers r and r + 4 of tile mm leaves, in lane j + 16 q, edge j
+  // (register r) and edge 16 + j (register r + 4) at hidden 32 mm + fperm(r) +
+  // off(q), off = 0, 8, 4, 12: the A operands of edge blocks 0 and 1.
+  f32x4 yb[2];
+  yb[0] = zero4();
+  yb[1] = zero4();
   {
-    const float* mr = &msm[s < NLM ? s : 0][4 * h];
+    const int j = s & 15, qk = (s >> 4) + 2 * h;
+    const float* mrow = &msm[j][8 * (qk & 1) + 4 * (qk >> 1)];
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const float bv = s < NLM ? mr[hid_k0(ks)] : 0.f;
-      yb = mfma32(s2[ks >> 4][ks & 15], bv, yb);
-    }
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int rr = 0; rr < 12; rr = (rr == 3 ? 8 : rr + 1)) {
+        float lo = s2[mm][rr], hi = s2[mm][rr + 4];
+        swap_rows16(lo, hi);
+        const float bv = mrow[32 * mm + fperm(rr)];
+        yb[0] = mfma16(lo, bv, yb[0]);
+        yb[1] = mfma16(hi, bv, yb[1]);
+      }
     pipeline_lds_mfma<32, 2, 6>();
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -370,10 +391,14 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
     pipeline_lds_mfma<16, 2, 6>();
   }
   __builtin_amdgcn_sched_barrier(0);
-  // Ybar to the lanes that own the edges, contracted with the harmonic gradients
-  if (s < NLM) {
+  // Ybar to the lanes that own the edges (block b register i of lane l: edge
+  // 16 b + 4 (l / 16) + i, harmonic l % 16), contracted with the harmonic gradients
+  {
+    const int l = s + 32 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ybsm[fperm(r) + 4 * h][s] = yb[r];
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ybsm[16 * b + 4 * (l >> 4) + i][l & 15] = yb[b][i];
   }
   wave_sync_lds();
   float G[3];
@@ -508,18 +533,18 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     int s = lane & 31, h = lane >> 5;
     asm volatile("" : "+v"(s), "+v"(h));
     const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
-    f32x16 T[2];
-    T[0] = zero16();
-    T[1] = zero16();
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
     const Recv xi = recv_pos(in, i);
     float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
     for (int q0 = qa; q0 < qb; q0 += 32)
       fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
     float acc[CPL][NLM];
     if (W3L)
-      unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, s, h, acc);
+      unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, acc);
     else
-      unit_last_layer<C, 4 * C>(T, L.tsm, W3, lane, s, h, acc);
+      unit_last_layer<C, 4 * C>(T, L.tsm, W3, lane, acc);
     // E_i = sum_c w_c sum_lm A^2 and dE/dA h = 2 w_c A h_c, A = h_c acc
     float esum = 0.f;
 #pragma unroll
@@ -641,7 +666,6 @@ void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, 
                           Box box, double cutoff, const int32_t* species, const eec_model* m,
                           const float* Abar, float* gout, char* ws) {
   if (p.N == 0 || p.E == 0) return;
-  launch_transpose_w3(s, p, m, ws);
   const float* W3T = (const float*)(ws + p.off_w3t);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
