@@ -226,21 +226,21 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * eec_energy_forces_folded (EEC_VARIANT_FOLDED), with hipEvent_t handles
  * (created by the caller, e.g. with hipEventCreate) recorded on `stream` around
  * each phase: events[2k] before and events[2k+1] after phase k, for
- *   k = EEC_PHASE_PREPARE   receiver index and pair grouping (folded, one
- *                           species: the transpose of W3 for C != 64 only),
+ *   k = EEC_PHASE_PREPARE   receiver index and pair grouping, and for the
+ *                           folded variant the transpose of W3 (folded, one
+ *                           species: that transpose for C != 64 only),
  *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
  *                           radial-row chunks and message passes; folded,
  *                           one species: the single fused kernel launch,
  *                           forward and backward),
  *       EEC_PHASE_READOUT   per-atom energies and dE/dA (folded, one
  *                           species: empty),
- *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch; the
- *                           folded variant also transposes W3 first; folded,
- *                           one species: empty),
+ *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch;
+ *                           folded, one species: empty),
  *       EEC_PHASE_SCATTER   forces and the energy total in one kernel launch
  *                           (with the virial, a second launch totals both).
- * `events` holds 2 * EEC_N_PHASES handles; NULL records nothing.  Results are
- * bit for bit those of the untimed call. */
+ * `events` holds 2 * EEC_N_PHASES handles (a NULL entry skips that record);
+ * NULL records nothing.  Results are bit for bit those of the untimed call. */
 enum { EEC_PHASE_PREPARE = 0, EEC_PHASE_FORWARD = 1, EEC_PHASE_READOUT = 2,
        EEC_PHASE_BACKWARD = 3, EEC_PHASE_SCATTER = 4, EEC_N_PHASES = 5 };
 enum { EEC_VARIANT_DIRECT = 0, EEC_VARIANT_FOLDED = 1 };
