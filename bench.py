@@ -22,7 +22,9 @@ Also reported:
                 its launch duration measured with hipEvents recorded by the
                 library on the stream it launches on; its algorithmic flops
                 (dominant_kernel; recomputation excluded) over that duration,
-                against the FP32 matrix peak;
+                against the FP32 matrix peak; `traffic` the HBM bytes per
+                launch from the recorded counter runs (recorded_traffic), or
+                null when the kernel has changed since they were taken;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
                 (all receivers of the cell: their forward and force backward),
                 on the host cores.
@@ -71,6 +73,34 @@ WORKLOADS = {
     "PV": "cubic perovskite 10x10x10 cells, 5000 atoms, 3 species, a=3.95 A, rc=6.0 A, C=64",
     "D32k": "diamond 16x16x16 conventional cells, 32768 atoms, rc=6.0 A, C=128",
 }
+
+
+def sources_digest() -> str:
+    """SHA-256 over the kernel sources (csrc/*.hip, csrc/*.hpp, by name)."""
+    import hashlib
+    src = os.path.join(ROOT, "equivariant_edge_convolution_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(src)):
+        if fn.endswith((".hip", ".hpp")):
+            h.update(fn.encode())
+            with open(os.path.join(src, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, config_name: str):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE / WRITE_SIZE
+    counter runs recorded in profiles/hbm_traffic.json, scaled by the copy
+    calibration there; None unless the record is for this workload and the
+    kernel sources are still the ones that were counted."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("workload") != config_name or rec.get("sources_sha256") != sources_digest():
+        return None
+    return float(rec["bytes_per_launch"])
 
 
 def cpu_baseline(cfg, n_rows: int = 1 << 30):
@@ -254,7 +284,8 @@ def main() -> int:
                    "n_edges": E, "channels": cfg.model.channels, "n_species": cfg.model.n_species},
         "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                     "traffic": recorded_traffic(kernel, args.config),
                      "flop_per_launch": flop, "launch_ms": launch_ms},
         "variant": args.variant,
         "variants": {} if args.no_other_variant else {
