@@ -3,6 +3,8 @@
 Tolerances: energy within 1e-5 relative; forces max|dF| <= 1e-4 RMS(F);
 every output finite.  The message A is compared to 2e-5 of its largest
 magnitude (float32 sums of <= 158 products of O(1) terms)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -45,6 +47,32 @@ def test_energy_forces_elementwise(name, variant):
     assert np.abs(got["forces"] - F0).max() <= 1e-4 * rms(F0)
     W0 = ref["virial"]
     assert np.abs(got["virial"] - W0).max() <= 1e-4 * np.abs(W0).max()
+
+
+_DENSE_REF = {}
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("cutoff", [6.5, 7.5])
+def test_dense_rows(cutoff, variant):
+    # rows of 6 (rc 6.5: 190 edges) and 10 (rc 7.5: 292-296 edges) tiles of 32:
+    # the folded one-species kernel keeps the first six tiles of a row for its
+    # backward and recomputes the rest, so both branches run; the cell side is
+    # below 2 rc (several images of one atom)
+    say(f"[energy_forces] dense D512 rc={cutoff} {variant}")
+    base = I.make_config("D512")
+    cfg = dataclasses.replace(base, model=dataclasses.replace(base.model, cutoff=cutoff))
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    deg = np.diff(np_(g.row_ptr))
+    assert deg.max() > 6 * 32 if cutoff > 7 else 5 * 32 < deg.max() <= 6 * 32
+    out = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, variant=variant).items()}
+    if cutoff not in _DENSE_REF:
+        _DENSE_REF[cutoff] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+    ref = _DENSE_REF[cutoff]
+    assert abs(float(out["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(out["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(out["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
 
 
 @pytest.mark.parametrize("name", ["D64", "PV3", "D512", "D64c128"])
