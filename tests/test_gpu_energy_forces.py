@@ -88,6 +88,32 @@ def test_edge_message(name):
     assert np.abs(A - A0).max() <= 2e-5 * np.abs(A0).max()
 
 
+@pytest.mark.parametrize("name", ["D4096", "D32k"])
+def test_edge_message_full_size_sampled(name):
+    # several streamed chunks with a ragged last one: rows that straddle a
+    # chunk boundary are first assigned, then accumulated; compared on every
+    # row that holds an edge index divisible by 32,768 plus a seeded sample
+    say(f"[edge_message] {name} sampled rows")
+    cfg = I.make_config(name)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    A = np_(B.edge_message(g, pos, cfg.box, species, model))
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    rp = csr.row_ptr.astype(np.int64)
+    marks = np.arange(32768, csr.n_edges, 32768)
+    rows = np.unique(np.concatenate([np.searchsorted(rp, marks, side="right") - 1,
+                                     np.random.default_rng(5).choice(cfg.n_atoms, 32, replace=False)]))
+    recv = csr.receivers()
+    h = cfg.model.emb.astype(np.float64)
+    for i in rows:
+        e = np.arange(rp[i], rp[i + 1])
+        d = (cfg.pos[csr.col[e]] - cfg.pos[recv[e]]) + csr.shift[e].astype(np.float64) * cfg.box[None, :]
+        pairs = cfg.species[recv[e]].astype(np.int64) * cfg.model.n_species + cfg.species[csr.col[e]]
+        msg, _ = M.edge_messages(d, pairs, h[cfg.species[csr.col[e]]], cfg.model)
+        A0 = msg.sum(axis=0)
+        assert np.abs(A[i] - A0).max() <= 2e-5 * np.abs(A0).max(), i
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("name,n_e,n_f", [("D4096", 256, 3), ("RS", 256, 6), ("PV", 256, 4), ("D32k", 96, 2)])
 def test_full_size_sampled(name, n_e, n_f, variant):
