@@ -50,18 +50,18 @@ PEAK_HBM_GBS = 8000.0
 #         (2 * 16 * 64 * 64 = 131,072).
 BWD_FLOP_PER_EDGE = {"direct": 45056 + 2304 + 2048, "folded": 2048 + 2048 + 8192 + 4096}
 BWD_FLOP_PER_UNIT = {"direct": 0, "folded": 2 * 16 * 64 * 64}
-# Forward of the folded path, for its one-species fused kernel (forward and
-# backward in one launch): per edge W1 (4,096) + W2 (8,192) + T = s2 Y^T
-# (2,048); per unit A = h T^T W3 (131,072).
+# The one-species fused kernel (forward and backward in one launch): per edge
+# the forward W1 (4,096) + W2 (8,192) + T = s2 Y^T (2,048) and the backward
+# (BWD_FLOP_PER_EDGE["folded"]); per receiver M = G T through the readout's
+# Gram matrices (2 * 16 * 64 * 64) and E_i = T . M / 2 (2 * 16 * 64).
 FOLD_FWD_FLOP_PER_EDGE = 4096 + 8192 + 2048
-FOLD_FWD_FLOP_PER_UNIT = 2 * 16 * 64 * 64
+FUSED_FLOP_PER_UNIT = 2 * 16 * 64 * 64 + 2 * 16 * 64
 
 
 def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int):
     """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
     if variant == "folded" and n_species == 1:
-        flop = ((FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges
-                + (FOLD_FWD_FLOP_PER_UNIT + BWD_FLOP_PER_UNIT["folded"]) * n_units)
+        flop = (FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges + FUSED_FLOP_PER_UNIT * n_units
         return "k_fold_fused", "forward", flop
     flop = BWD_FLOP_PER_EDGE[variant] * n_edges + BWD_FLOP_PER_UNIT[variant] * n_units
     return ("k_backward" if variant == "direct" else "k_fold_backward"), "backward", flop

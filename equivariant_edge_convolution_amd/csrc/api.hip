@@ -269,7 +269,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   if (folded && fold_fused_supported(p)) {
     // one kernel per receiver from geometry to dE/dd; no preparation, no A
     mark(2 * EEC_PHASE_PREPARE);
-    if (fold_fused_needs_w3t(p)) launch_transpose_w3(s, p, m, ws);
+    launch_gram(s, p, m, ws);
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);
     launch_fold_fused(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws);

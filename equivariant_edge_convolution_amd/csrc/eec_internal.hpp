@@ -110,11 +110,11 @@ size_t fold_stash_bytes(const ConvPlan& p);
 void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);
 
 // One species: the whole folded call per receiver in one kernel (forward tiles,
-// A_i, E_i into ei, dE/dA_i, backward tiles into gout).  When
-// fold_fused_needs_w3t, reads the transposed last-layer weights
-// launch_transpose_w3 wrote.
+// T_i, E_i into ei and M_i through the Gram matrices of the quadratic readout,
+// backward tiles into gout).  launch_gram writes those matrices (64 KB, in the
+// transposed-weights slot of the workspace) first on the stream.
 bool fold_fused_supported(const ConvPlan& p);
-bool fold_fused_needs_w3t(const ConvPlan& p);
+void launch_gram(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
                        char* ws);

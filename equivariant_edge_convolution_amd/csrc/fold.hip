@@ -24,16 +24,16 @@ using namespace chain;
 // Every unit belongs to one wave; its LDS region holds, in turn,
 //   forward:  ysm [32][17] harmonics of the tile's edges (zero rows for padding),
 //             tsm [64][16] T of the unit, staged for the last layer;
-//   backward: ahsm [C][AHS] dE/dA_{lm,c} h_c by channel row, then (written once
-//             every ahsm row has been read) msm [16][65] M of the unit, and
-//             ybsm [32][17] dE/dY of the tile's edges.
+//   backward: ahsm [C][AHS] dE/dA_{lm,c} h_c by channel row (several species),
+//             then (written once every ahsm or tsm row has been read) msm
+//             [16][65] M of the unit, and ybsm [32][17] dE/dY of the tile's edges.
 constexpr int AHS = NLM + 4;  // row stride of the staged dE/dA h rows (16-byte aligned)
 template <int C>
 struct FoldLds {
   static constexpr int YSM = 0, TSM = 32 * (NLM + 1), FWD = TSM + HID * NLM;
   static constexpr int AHSM = 0, MSM = 0, YBSM = NLM * (HID + 1), BWD_M = YBSM + 32 * (NLM + 1);
   static constexpr int BWD = C * AHS > BWD_M ? C * AHS : BWD_M;
-  static constexpr int FWD_ONLY = FWD, BWD_ONLY = BWD, FUSED = FWD > BWD ? FWD : BWD;
+  static constexpr int FWD_ONLY = FWD, BWD_ONLY = BWD, FUSED = FWD > BWD_M ? FWD : BWD_M;
 };
 
 template <int C>
@@ -500,32 +500,46 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
 // ------------------------------------------------------------------ fused (one species)
 // With one species, receiver i's unit holds its whole row, and the backward of
 // the unit needs only M_i, which depends on nothing but the unit's own forward:
-// one wave runs forward tiles -> A_i -> E_i and dE/dA_i h -> M_i -> backward
-// tiles, so A never leaves the chip and the readout needs no kernel of its own.
-// (The forward's activations are recomputed in the backward tiles: keeping them
-// would cost a round trip of 3 x 64 floats per edge through HBM, more than the
-// two layers take to redo.)  With W3L the last layer's weights sit in LDS too
-// (C = 64: 64 KB), read along rows for A and down columns for M, so neither
-// needs the transposed copy and the units of a workgroup share one read of W3.
-template <int C, int W, bool W3L>
+// one wave runs forward tiles -> T_i -> E_i and M_i -> backward tiles.  The
+// quadratic readout needs no A at all: with A_{lm,c} = h_c sum_k W3[k, lC+c]
+// T_{lm,k} and E_i = sum_c w_c sum_lm A^2, the per-degree Gram matrices
+//   G_l[k][k'] = sum_c 2 w_c h_c^2 W3[k][lC+c] W3[k'][lC+c]     (k_gram, per call)
+// give M_{lm} = G_{l(lm)} T_{lm} and E_i = 1/2 sum_lm T_{lm} . M_{lm}: one
+// 64 x 64 contraction per harmonic per receiver, whatever C is, instead of A
+// (16 x 64 x C) and M (16 x C x 64).  G (64 KB) sits in LDS beside W1 and W2.
+constexpr int LDG = HID + 1;                       // row stride of G_l in LDS
+constexpr int GRAM_FLOATS = 4 * HID * LDG;
+
+// G_l[k][k'] for one species pair: block (l, k), thread k'; binary64 sums.
+__global__ void __launch_bounds__(64) k_gram(int C, const float* __restrict__ W3, const float* __restrict__ emb,
+                                             const float* __restrict__ w_read, float* __restrict__ G) {
+  const int l = blockIdx.x >> 6, k = blockIdx.x & 63, kk = threadIdx.x;
+  const float* a = W3 + (size_t)k * 4 * C + l * C;
+  const float* b = W3 + (size_t)kk * 4 * C + l * C;
+  double acc = 0.0;
+  for (int c = 0; c < C; ++c) {
+    const double hc = emb[c];
+    acc += 2.0 * (double)w_read[c] * hc * hc * (double)a[c] * (double)b[c];
+  }
+  G[((size_t)l * HID + k) * HID + kk] = (float)acc;
+}
+
+template <int C, int W>
 __global__ void __launch_bounds__(64 * W)
 k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
-             const float* __restrict__ W3, const float* __restrict__ W3T, const float* __restrict__ emb,
-             const float* __restrict__ w_read, float* __restrict__ ei, float* __restrict__ gout,
+             const float* __restrict__ G, float* __restrict__ ei, float* __restrict__ gout,
              float* __restrict__ stash) {
-  constexpr int CPL = C / 64;
-  __shared__ float wl[W3L ? Lds<C>::FLOATS : W12_FLOATS];
+  __shared__ float wl[W12_FLOATS + GRAM_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
-  const float* w1s = wl + Lds<C>::W1;
-  const float* w2s = wl + Lds<C>::W2;
+  const float* w1s = wl;
+  const float* w2s = wl + NB * LDH;
+  float* gs = wl + W12_FLOATS;
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  if (W3L)
-    stage_weights<C>(wl, W1, W2, W3, 0);
-  else
-    stage_w12(wl, W1, W2, 0);
+  stage_w12(wl, W1, W2, 0);
+  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) gs[(t >> 6) * LDG + (t & 63)] = G[t];
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
@@ -540,34 +554,49 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
     for (int q0 = qa; q0 < qb; q0 += 32)
       fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
-    float acc[CPL][NLM];
-    if (W3L)
-      unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, acc);
-    else
-      unit_last_layer<C, 4 * C>(T, L.tsm, W3, lane, acc);
-    // E_i = sum_c w_c sum_lm A^2 and dE/dA h = 2 w_c A h_c, A = h_c acc
+    // T block b register r, lane l: hidden 16 b + 4 (l / 16) + r, harmonic l % 16
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
+    wave_sync_lds();
+    // M[lm][k] = sum_k' G_l(lm)[k][k'] T[k'][lm] and E_i = 1/2 sum T M (lane = hidden k)
+    float macc[NLM];
+#pragma unroll
+    for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
+    {
+      const float* g = gs + lane * LDG;
+#pragma unroll 4
+      for (int kk = 0; kk < HID; ++kk) {
+        float t[NLM];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 x = *reinterpret_cast<const float4*>(&L.tsm[kk][4 * v]);
+          t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
+        }
+        const float g0 = g[kk], g1 = g[HID * LDG + kk], g2 = g[2 * HID * LDG + kk], g3 = g[3 * HID * LDG + kk];
+        macc[0] += g0 * t[0];
+#pragma unroll
+        for (int lm = 1; lm < 4; ++lm) macc[lm] += g1 * t[lm];
+#pragma unroll
+        for (int lm = 4; lm < 9; ++lm) macc[lm] += g2 * t[lm];
+#pragma unroll
+        for (int lm = 9; lm < 16; ++lm) macc[lm] += g3 * t[lm];
+      }
+    }
     float esum = 0.f;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int c = lane + 64 * q;
-      const float hc = emb[c], wc = w_read[c];
-      float sq = 0.f;
-#pragma unroll
-      for (int k = 0; k < NLM; ++k) {
-        const float av = hc * acc[q][k];
-        sq += av * av;
-        L.ahsm[c][k] = 2.f * wc * av * hc;
-      }
-      esum += wc * sq;
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(&L.tsm[lane][4 * v]);
+      esum += x.x * macc[4 * v] + x.y * macc[4 * v + 1] + x.z * macc[4 * v + 2] + x.w * macc[4 * v + 3];
     }
     for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
-    if (lane == 0) ei[i] = esum;
+    if (lane == 0) ei[i] = 0.5f * esum;
     if (qb <= qa) continue;
+    wave_sync_lds();  // msm overlays tsm
+#pragma unroll
+    for (int lm = 0; lm < NLM; ++lm) L.msm[lm][lane] = macc[lm];
     wave_sync_lds();
-    if (W3L)
-      unit_M<C, 1>(L.ahsm, wl + Lds<C>::W3 + lane * Lds<C>::LD3, lane, L.msm);
-    else
-      unit_M<C, HID>(L.ahsm, W3T + lane, lane, L.msm);
     for (int q0 = qa; q0 < qb; q0 += 32)
       bwd_tile(in, xi, nullptr, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
   }
@@ -644,22 +673,23 @@ void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, c
 }
 
 bool fold_fused_supported(const ConvPlan& p) { return p.S == 1; }
-bool fold_fused_needs_w3t(const ConvPlan& p) { return p.C != 64; }
+
+void launch_gram(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws) {
+  k_gram<<<4 * HID, HID, 0, s>>>(p.C, m->W3, m->emb, m->w_read, (float*)(ws + p.off_w3t));
+}
 
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
                        char* ws) {
   if (p.N == 0) return;
-  const float* W3T = (const float*)(ws + p.off_w3t);
+  const float* G = (const float*)(ws + p.off_w3t);
   float* stash = (float*)(ws + p.off_stash);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
   if (p.C == 64)
-    k_fold_fused<64, WAVES, true><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, nullptr, m->emb,
-                                                                       m->w_read, ei, gout, stash);
+    k_fold_fused<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
   else
-    k_fold_fused<128, WAVES, false><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, m->W3, W3T, m->emb,
-                                                                         m->w_read, ei, gout, stash);
+    k_fold_fused<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
 }
 
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

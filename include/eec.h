@@ -212,9 +212,12 @@ EEC_API eec_status eec_energy_forces(void *stream, const eec_graph *g, const dou
  *   backward: M_{i,s}[lm][k] = sum_c (dE/dA_i)[lm][c] h_{s,c} W3_{(Z_i,s)}[k][l C + c],
  *             dE/dY_e = M s2_e,  dE/ds2_e = M^T Y_e.
  * The per-edge radial weights R are never formed.  With one species the
- * whole call per receiver (forward tiles, A_i, E_i, dE/dA_i, backward tiles)
- * runs in one kernel and A never leaves the chip.  Arguments as
- * eec_energy_forces; same workspace size. */
+ * whole call per receiver runs in one kernel, and the quadratic readout is
+ * taken through per-degree Gram matrices
+ *   G_l[k][k'] = sum_c 2 w_c h_c^2 W3[k][lC+c] W3[k'][lC+c]:
+ *   M_i[lm] = G_l(lm) T_i[lm],  E_i = 1/2 sum_lm T_i[lm] . M_i[lm],
+ * so A is never formed either.  Arguments as eec_energy_forces; same
+ * workspace size. */
 EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, const double *pos,
                                     const double *box /*[host][3]*/, const int32_t *species,
                                     const eec_model *m, float *energy, float *atom_energy,

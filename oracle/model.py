@@ -313,16 +313,12 @@ def message_h_folded(d, csr: CSR, species, model):
     return A
 
 
-def message_reassociated(d, csr: CSR, species, model):
-    """A with the linear last layer moved past the edge sum:
-    T_{i,s,lm,k} = sum_{e in row i, Z_j = s} Y_{e,lm} s2_{e,k},
-    A_{i,lm,c} = sum_s h_{s,c} sum_k W3^{(Z_i,s)}[k, lC+c] T_{i,s,lm,k}."""
-    C = model.channels
+def reassociated_T(d, csr: CSR, species, model):
+    """T_{i,s,lm,k} = sum_{e in row i, Z_j = s} Y_{e,lm} s2_{e,k}  [n, S, 16, 64]."""
     S = model.n_species
     n = len(csr.row_ptr) - 1
     pairs = pair_index(species, csr, S)
     recv = csr.receivers()
-    h = _f64(model.emb)
     T = np.zeros((n, S, 16, 64))
     rp = csr.row_ptr.astype(np.int64)
     for i0, i1 in _blocks(csr.row_ptr):
@@ -337,6 +333,18 @@ def message_reassociated(d, csr: CSR, species, model):
             if not np.any(sel):
                 continue
             T[i0:i1, s] += _segment_sum(outer[sel], recv[e0:e1][sel] - i0, i1 - i0)
+    return T
+
+
+def message_reassociated(d, csr: CSR, species, model):
+    """A with the linear last layer moved past the edge sum:
+    T_{i,s,lm,k} = sum_{e in row i, Z_j = s} Y_{e,lm} s2_{e,k},
+    A_{i,lm,c} = sum_s h_{s,c} sum_k W3^{(Z_i,s)}[k, lC+c] T_{i,s,lm,k}."""
+    C = model.channels
+    S = model.n_species
+    n = len(csr.row_ptr) - 1
+    h = _f64(model.emb)
+    T = reassociated_T(d, csr, species, model)
     A = np.zeros((n, 16, C))
     for i in range(n):
         zi = species[i]
@@ -369,6 +377,25 @@ def backward_reassociated_terms(d, csr: CSR, species, model, A):
     Ybar = np.einsum("emk,ek->em", Me, st["s2"])
     s2bar = np.einsum("emk,em->ek", Me, st["Y"])
     return Ybar, s2bar
+
+
+def gram_readout(d, csr: CSR, species, model):
+    """One species: the quadratic readout and its dE/dA pulled back to T without
+    forming A.  With A_{lm,c} = h_c sum_k W3[k, lC+c] T_{lm,k} and
+    E_i = sum_c w_c sum_lm A_{lm,c}^2, the per-degree Gram matrices
+    G_l[k, k'] = sum_c 2 w_c h_c^2 W3[k, lC+c] W3[k', lC+c]
+    give M_{i,lm} = G_{l(lm)} T_{i,lm} (the matrix of backward_reassociated_terms)
+    and E_i = 1/2 sum_lm T_{i,lm} . M_{i,lm}.  Returns (E_i [n], M [n, 16, 64])."""
+    if model.n_species != 1:
+        raise ValueError("gram_readout is the one-species form")
+    C = model.channels
+    T = reassociated_T(d, csr, species, model)[:, 0]  # [n, 16, 64]
+    W3 = _f64(model.W3[0]).reshape(64, 4, C)  # [k, l, c]
+    wh2 = 2.0 * _f64(model.w_read) * _f64(model.emb[0]) ** 2
+    G = np.einsum("klc,c,jlc->lkj", W3, wh2, W3)  # [4, 64, 64]
+    M = np.einsum("mkj,nmj->nmk", G[LIDX], T)
+    Ei = 0.5 * np.einsum("nmk,nmk->n", T, M)
+    return Ei, M
 
 
 def backward_direct_terms(d, csr: CSR, species, model, A):

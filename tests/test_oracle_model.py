@@ -259,6 +259,26 @@ def test_folded_and_reassociated_last_layer(name):
     assert np.abs(sr - sd).max() <= 1e-12 * np.abs(sd).max()
 
 
+@pytest.mark.parametrize("name", ["D64", "D64c128"])
+def test_gram_readout(name):
+    # E_i and dE/dA pulled back to T through per-degree Gram matrices, with no A:
+    # equal to the unfolded chain's E_i and its Ybar, s2bar
+    cfg = I.make_config(name)
+    m = cfg.model
+    csr = N.neighbors_celllist(cfg.pos, cfg.box, RC)
+    d = N.edge_vectors(cfg.pos, cfg.box, csr)
+    out = M.forward_edges(d, csr, cfg.species, m)
+    Ei, Mg = M.gram_readout(d, csr, cfg.species, m)
+    assert np.abs(Ei - out["Ei"]).max() <= 1e-12 * np.abs(out["Ei"]).max()
+    yd, sd = M.backward_direct_terms(d, csr, cfg.species, m, out["A"])
+    st = M._edge_stage(d, M.pair_index(cfg.species, csr, 1), m, m.cutoff)
+    Me = Mg[csr.receivers()]
+    yg = np.einsum("emk,ek->em", Me, st["s2"])
+    sg = np.einsum("emk,em->ek", Me, st["Y"])
+    assert np.abs(yg - yd).max() <= 1e-12 * np.abs(yd).max()
+    assert np.abs(sg - sd).max() <= 1e-12 * np.abs(sd).max()
+
+
 def test_edge_direction_reading_only_flips_odd_degrees():
     # reversing every edge vector flips odd-l A and leaves E unchanged
     cfg = I.make_config("D64")

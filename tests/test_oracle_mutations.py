@@ -178,3 +178,31 @@ def test_fold_with_receiver_species_weights(monkeypatch):
 
     monkeypatch.setattr(M, "message_reassociated", bad)
     _fails(TM.test_folded_and_reassociated_last_layer, "RS2")
+
+
+def test_gram_without_the_factor_two(monkeypatch):
+    # the Gram matrices built from w h^2 instead of 2 w h^2 (the derivative's factor)
+    orig = M.gram_readout
+
+    def bad(d, csr, species, model):
+        Ei, Mg = orig(d, csr, species, model)
+        return Ei, 0.5 * Mg
+
+    monkeypatch.setattr(M, "gram_readout", bad)
+    _fails(TM.test_gram_readout, "D64")
+
+
+def test_gram_with_the_wrong_degree_block(monkeypatch):
+    # every harmonic paired with the l = 1 block of W3
+    orig_lidx = M.LIDX
+
+    def bad(d, csr, species, model):
+        monkeypatch.setattr(M, "LIDX", np.where(orig_lidx == 0, 0, 1))
+        try:
+            return M.__dict__["_gram_orig"](d, csr, species, model)
+        finally:
+            monkeypatch.setattr(M, "LIDX", orig_lidx)
+
+    monkeypatch.setattr(M, "_gram_orig", M.gram_readout, raising=False)
+    monkeypatch.setattr(M, "gram_readout", bad)
+    _fails(TM.test_gram_readout, "D64")
