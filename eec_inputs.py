@@ -72,6 +72,8 @@ CONFIGS = {
     "PV3": ("perovskite", 3, 64),
     "D64c128": ("diamond", 2, 128),
     "D512c128": ("diamond", 4, 128),
+    "D1728": ("diamond", 6, 64),
+    "D1728c128": ("diamond", 6, 128),
 }
 
 

@@ -497,6 +497,39 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
   }
 }
 
+// M_i and E_i from the staged T of the unit through the Gram matrices (lane =
+// hidden k).  G_l[k][k'] is read as g(l, k') for this lane's k.
+template <typename GF>
+__device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane, GF&& g, float macc[NLM]) {
+#pragma unroll
+  for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
+#pragma unroll 4
+  for (int kk = 0; kk < HID; ++kk) {
+    float t[NLM];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(&tsm[kk][4 * v]);
+      t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
+    }
+    const float g0 = g(0, kk), g1 = g(1, kk), g2 = g(2, kk), g3 = g(3, kk);
+    macc[0] += g0 * t[0];
+#pragma unroll
+    for (int lm = 1; lm < 4; ++lm) macc[lm] += g1 * t[lm];
+#pragma unroll
+    for (int lm = 4; lm < 9; ++lm) macc[lm] += g2 * t[lm];
+#pragma unroll
+    for (int lm = 9; lm < 16; ++lm) macc[lm] += g3 * t[lm];
+  }
+  float esum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float4 x = *reinterpret_cast<const float4*>(&tsm[lane][4 * v]);
+    esum += x.x * macc[4 * v] + x.y * macc[4 * v + 1] + x.z * macc[4 * v + 2] + x.w * macc[4 * v + 3];
+  }
+  for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
+  return 0.5f * esum;
+}
+
 // ------------------------------------------------------------------ fused (one species)
 // With one species, receiver i's unit holds its whole row, and the backward of
 // the unit needs only M_i, which depends on nothing but the unit's own forward:
@@ -562,36 +595,9 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     wave_sync_lds();
     // M[lm][k] = sum_k' G_l(lm)[k][k'] T[k'][lm] and E_i = 1/2 sum T M (lane = hidden k)
     float macc[NLM];
-#pragma unroll
-    for (int lm = 0; lm < NLM; ++lm) macc[lm] = 0.f;
-    {
-      const float* g = gs + lane * LDG;
-#pragma unroll 4
-      for (int kk = 0; kk < HID; ++kk) {
-        float t[NLM];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4 x = *reinterpret_cast<const float4*>(&L.tsm[kk][4 * v]);
-          t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
-        }
-        const float g0 = g[kk], g1 = g[HID * LDG + kk], g2 = g[2 * HID * LDG + kk], g3 = g[3 * HID * LDG + kk];
-        macc[0] += g0 * t[0];
-#pragma unroll
-        for (int lm = 1; lm < 4; ++lm) macc[lm] += g1 * t[lm];
-#pragma unroll
-        for (int lm = 4; lm < 9; ++lm) macc[lm] += g2 * t[lm];
-#pragma unroll
-        for (int lm = 9; lm < 16; ++lm) macc[lm] += g3 * t[lm];
-      }
-    }
-    float esum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 x = *reinterpret_cast<const float4*>(&L.tsm[lane][4 * v]);
-      esum += x.x * macc[4 * v] + x.y * macc[4 * v + 1] + x.z * macc[4 * v + 2] + x.w * macc[4 * v + 3];
-    }
-    for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
-    if (lane == 0) ei[i] = 0.5f * esum;
+    const float* g = gs + lane * LDG;
+    const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return g[l * HID * LDG + kk]; }, macc);
+    if (lane == 0) ei[i] = e2;
     if (qb <= qa) continue;
     wave_sync_lds();  // msm overlays tsm
 #pragma unroll
@@ -599,6 +605,74 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     wave_sync_lds();
     for (int q0 = qa; q0 < qb; q0 += 32)
       bwd_tile(in, xi, nullptr, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
+  }
+}
+
+// ------------------------------------------------------------------ split (one species, few receivers)
+// With fewer receivers than the chip has wave slots, one wave per receiver
+// leaves most CUs idle and one receiver's tiles in sequence are the whole
+// call.  Here a workgroup takes a receiver and its W waves share the row's
+// tiles (wave w: tiles w, w + W, ...): each sums its partial T, the first wave
+// adds them up in LDS and forms M and E_i from G in global memory (G is
+// symmetric, so lane k reads G_l[k'][k] along a row), and every wave runs the
+// backward of its own tiles from its own stash rows.
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
+             const float* __restrict__ G, float* __restrict__ ei, float* __restrict__ gout,
+             float* __restrict__ stash) {
+  __shared__ float w12[W12_FLOATS];
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
+  __shared__ __align__(16) float msh[NLM][HID + 1];  // M of the receiver, read by every wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const WaveLds<C> L(wbuf[wave]);
+  const float* w1s = w12;
+  const float* w2s = w12 + NB * LDH;
+  const int N = un.n_atoms;
+  stage_w12(w12, W1, W2, 0);
+  __syncthreads();
+  float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+  for (int i = blockIdx.x; i < N; i += gridDim.x) {
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
+    const Recv xi = recv_pos(in, i);
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
+    int j = 0;
+    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
+      fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
+               j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
+    __syncthreads();
+    if (wave == 0) {
+      // T = sum of the waves' partials, in wave order (lane: 16 consecutive entries)
+      float* tw = &L.tsm[0][0];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = tw[16 * lane + e];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += wbuf[w][FoldLds<C>::TSM + 16 * lane + e];
+        tw[16 * lane + e] = v;
+      }
+      wave_sync_lds();
+      float macc[NLM];
+      const float* gl = G + lane;
+      const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return gl[(l * HID + kk) * HID]; }, macc);
+      if (lane == 0) ei[i] = e2;
+#pragma unroll
+      for (int lm = 0; lm < NLM; ++lm) msh[lm][lane] = macc[lm];
+    }
+    __syncthreads();
+    j = 0;
+    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
+      bwd_tile(in, xi, nullptr, w1s, w2s, msh, L.ybsm, q0, qa, qb, s, h, gout,
+               j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+    __syncthreads();  // msh and the wave buffers are rewritten for the next receiver
   }
 }
 
@@ -647,11 +721,18 @@ int unit_grid(const ConvPlan& p) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(batches, 256));
 }
 
+// One species and at most this many receivers: a workgroup per receiver
+// (k_fold_split) instead of a wave per receiver (k_fold_fused).
+constexpr int SPLIT_MAX_ATOMS = 768;  // past it a wave per receiver is faster (measured)
+bool use_split(const ConvPlan& p) { return p.N <= SPLIT_MAX_ATOMS; }
+int split_grid(const ConvPlan& p) { return std::max(1, std::min(p.N, 256)); }
+
 }  // namespace
 
 size_t fold_stash_bytes(const ConvPlan& p) {
   if (p.S != 1) return 0;
-  return sizeof(float) * (size_t)unit_grid(p) * WAVES * STASH_TILES * 32 * ZROW;
+  const int waves = use_split(p) ? split_grid(p) * WAVES : unit_grid(p) * WAVES;
+  return sizeof(float) * (size_t)waves * STASH_TILES * 32 * ZROW;
 }
 
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
@@ -686,10 +767,16 @@ void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
   float* stash = (float*)(ws + p.off_stash);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
-  if (p.C == 64)
+  if (use_split(p)) {
+    if (p.C == 64)
+      k_fold_split<64, WAVES><<<split_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
+    else
+      k_fold_split<128, WAVES><<<split_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
+  } else if (p.C == 64) {
     k_fold_fused<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
-  else
+  } else {
     k_fold_fused<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, m->W1, m->W2, G, ei, gout, stash);
+  }
 }
 
 void launch_fold_backward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

@@ -52,6 +52,24 @@ def test_energy_forces_elementwise(name, variant):
 _DENSE_REF = {}
 
 
+_MID_REF = {}
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", ["D1728", "D1728c128"])
+def test_energy_forces_elementwise_wave_per_receiver(name, variant):
+    # 1,728 receivers: above the size where the folded one-species call takes a
+    # workgroup per receiver, so this is the wave-per-receiver fused kernel
+    say(f"[energy_forces] {name} {variant}")
+    cfg, *_, got = _run(name, variant=variant)
+    if name not in _MID_REF:
+        _MID_REF[name] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+    ref = _MID_REF[name]
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("cutoff", [6.5, 7.5])
 def test_dense_rows(cutoff, variant):
@@ -152,8 +170,11 @@ def test_full_energy_headline_cell():
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_bitwise_repeatable(variant):
-    cfg = I.make_config("PV3")
+@pytest.mark.parametrize("name", ["PV3", "D512", "D1728"])
+def test_bitwise_repeatable(variant, name):
+    # several species; one species with a workgroup per receiver; one species
+    # with a wave per receiver
+    cfg = I.make_config(name)
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
     ef = B.EnergyForces(g, model, pos.device, virial=True, variant=variant)
