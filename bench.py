@@ -56,13 +56,22 @@ BWD_FLOP_PER_UNIT = {"direct": 0, "folded": 2 * 16 * 64 * 64}
 # Gram matrices (2 * 16 * 64 * 64) and E_i = T . M / 2 (2 * 16 * 64).
 FOLD_FWD_FLOP_PER_EDGE = 4096 + 8192 + 2048
 FUSED_FLOP_PER_UNIT = 2 * 16 * 64 * 64 + 2 * 16 * 64
+# Several species (k_fold_multi): per (receiver, sender species) unit the
+# forward's A += h T^T W3 (2 * 16 * 64 * 64) and the backward's M.
+FOLD_FWD_FLOP_PER_UNIT = 2 * 16 * 64 * 64
 
 
-def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int):
+def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int, n_atoms: int = 1 << 30):
     """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
     if variant == "folded" and n_species == 1:
         flop = (FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges + FUSED_FLOP_PER_UNIT * n_units
-        return "k_fold_fused", "forward", flop
+        # up to 768 receivers the library gives each a workgroup (k_fold_split)
+        return ("k_fold_split" if n_atoms <= 768 else "k_fold_fused"), "forward", flop
+    if variant == "folded" and n_species <= 3:
+        # per (receiver, sender species) unit: A += h T^T W3 and M = (dE/dA h) W3^T
+        flop = ((FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges
+                + (FOLD_FWD_FLOP_PER_UNIT + BWD_FLOP_PER_UNIT["folded"]) * n_units)
+        return "k_fold_multi", "forward", flop
     flop = BWD_FLOP_PER_EDGE[variant] * n_edges + BWD_FLOP_PER_UNIT[variant] * n_units
     return ("k_backward" if variant == "direct" else "k_fold_backward"), "backward", flop
 WORKLOADS = {
@@ -233,7 +242,7 @@ def main() -> int:
         kernel's launch only; then the same number of calls with every phase
         recorded (phases_ms, not part of the timed figure)."""
         ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=variant)
-        _, dom_phase, _ = dominant_kernel(variant, cfg.model.n_species, E, n_units)
+        _, dom_phase, _ = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
         dp = B.PHASES.index(dom_phase)
         ev = B.HipEvents(2 * nph * max(steps, 1))
         for _ in range(warmup):
@@ -263,7 +272,7 @@ def main() -> int:
         o_ms, o_phase, o_energy, o_dom = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
     def roof(variant, launch_ms):
-        kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units)
+        kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
         return kernel, flop, launch_ms, flop / (launch_ms * 1e-3) / 1e12
 
     kernel, flop, launch_ms, achieved = roof(args.variant, dom_ms)

@@ -283,6 +283,25 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     mark(2 * EEC_PHASE_SCATTER + 1);
     return launched("energy_forces");
   }
+  if (folded && fold_multi_supported(p)) {
+    // one kernel per call from geometry to dE/dd, sender species after species
+    mark(2 * EEC_PHASE_PREPARE);
+    launch_prepare(s, p, g, species, ws, nullptr);
+    launch_species_order(s, p, species, ws);
+    launch_transpose_w3(s, p, m, ws);
+    mark(2 * EEC_PHASE_PREPARE + 1);
+    mark(2 * EEC_PHASE_FORWARD);
+    launch_fold_multi(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws);
+    mark(2 * EEC_PHASE_FORWARD + 1);
+    for (int k : {EEC_PHASE_READOUT, EEC_PHASE_BACKWARD}) {
+      mark(2 * k);
+      mark(2 * k + 1);
+    }
+    mark(2 * EEC_PHASE_SCATTER);
+    launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
+    mark(2 * EEC_PHASE_SCATTER + 1);
+    return launched("energy_forces");
+  }
   mark(2 * EEC_PHASE_PREPARE);
   launch_prepare(s, p, g, species, ws, A);
   if (folded) launch_transpose_w3(s, p, m, ws);

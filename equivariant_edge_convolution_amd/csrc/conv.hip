@@ -163,6 +163,35 @@ __global__ void __launch_bounds__(256) k_seg_bounds(int32_t n, int S, const int3
   seg[2 * t + 1] = (int32_t)lo2;
 }
 
+// Atoms ordered by species, stably, and the species' offsets in that order
+// (zstart [S+1]): one workgroup, each thread a contiguous slice of atoms.
+constexpr int SO_T = 1024;
+__global__ void __launch_bounds__(SO_T) k_species_order(int32_t n, int S, const int32_t* __restrict__ species,
+                                                         int32_t* __restrict__ ord, int32_t* __restrict__ zstart) {
+  __shared__ int32_t cnt[4][SO_T + 1];
+  __shared__ int32_t base[5];
+  const int t = threadIdx.x;
+  const int per = (n + SO_T - 1) / SO_T;
+  const int a = min(n, t * per), b = min(n, a + per);
+  int c[4] = {0, 0, 0, 0};
+  for (int k = a; k < b; ++k) c[min(max(species[k], 0), S - 1)]++;
+  for (int z = 0; z < S; ++z) cnt[z][t + 1] = c[z];
+  if (t < S) cnt[t][0] = 0;
+  __syncthreads();
+  if (t < S)
+    for (int k = 1; k <= SO_T; ++k) cnt[t][k] += cnt[t][k - 1];
+  __syncthreads();
+  if (t == 0) {
+    base[0] = 0;
+    for (int z = 0; z < S; ++z) base[z + 1] = base[z] + cnt[z][SO_T];
+    for (int z = 0; z <= S; ++z) zstart[z] = base[z];
+  }
+  __syncthreads();
+  int pos[4];
+  for (int z = 0; z < S; ++z) pos[z] = base[z] + cnt[z][t];
+  for (int k = a; k < b; ++k) ord[pos[min(max(species[k], 0), S - 1)]++] = k;
+}
+
 // ------------------------------------------------------------ message
 // One workgroup of 4 waves per receiver; lanes over channels; each wave sums a
 // contiguous quarter of the receiver's edges inside the chunk in CSR order
@@ -459,6 +488,8 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
     p.off_pair_start = o; o += align256(8 * (size_t)(p.P + 1));
     p.off_blockcnt = o;   o += align256((4 + 8) * (size_t)p.P * std::max<int64_t>(p.n_count_blocks, 1));
     p.off_seg = o;        o += align256(8 * (size_t)p.S * N);
+    p.off_ord = o;        o += align256(4 * (size_t)N);
+    p.off_zstart = o;     o += 256;
   }
   p.off_A = o;     o += align256(4 * (size_t)p.S * N * NLM * p.C);  // S partial slabs
   p.off_R = o;     o += align256(4 * (size_t)p.chunk * p.NC);
@@ -492,6 +523,11 @@ void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
                                                                        pair_start, perm,
                                                                        (int32_t*)(ws + p.off_seg));
   }
+}
+
+void launch_species_order(hipStream_t s, const ConvPlan& p, const int32_t* species, char* ws) {
+  if (p.S > 4 || p.S < 2 || p.N == 0) return;
+  k_species_order<<<1, SO_T, 0, s>>>(p.N, p.S, species, (int32_t*)(ws + p.off_ord), (int32_t*)(ws + p.off_zstart));
 }
 
 void launch_message(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,

@@ -44,7 +44,7 @@ struct ConvPlan {
   int64_t chunk;  // edges per streamed chunk
   size_t bytes;
   size_t off_recv, off_perm, off_pair_start, off_blockcnt, off_seg, off_A, off_R, off_Y, off_g,
-      off_vpart, off_ei, off_w3t, off_stash;
+      off_vpart, off_ei, off_w3t, off_stash, off_ord, off_zstart;
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
@@ -52,6 +52,9 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
 // Graph preparation: receiver of each edge; pair-grouped edge order when S > 1.
 void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
                     char* ws, float* zero_rows_of /* [N][16][C] or NULL */);
+
+// Atoms in species order (stable) and the species' offsets, for 2 <= S <= 4.
+void launch_species_order(hipStream_t s, const ConvPlan& p, const int32_t* species, char* ws);
 
 // Radial network over a range of edges.  When `basis_in` is given the basis is
 // read from it (materialising entry point); otherwise it is computed from the
@@ -116,6 +119,14 @@ void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, c
 bool fold_fused_supported(const ConvPlan& p);
 void launch_gram(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws);
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
+                       char* ws);
+
+// Two or three species: the whole folded call per receiver in one kernel,
+// sender species after sender species (needs launch_prepare,
+// launch_species_order and launch_transpose_w3 first on the stream).
+bool fold_multi_supported(const ConvPlan& p);
+void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
                        char* ws);
 

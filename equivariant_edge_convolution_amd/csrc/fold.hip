@@ -676,6 +676,136 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   }
 }
 
+// ------------------------------------------------------------------ fused (several species)
+// Two or three species: one wave per receiver, workgroups taking batches of
+// receivers of one species (atoms in species order).  For each sender species
+// s in turn the workgroup stages the weights of pair (Z_i, s) in LDS and every
+// wave runs the forward tiles of its unit (s, i) and adds h_s T_s^T W3 to its
+// A; then E_i and dE/dA; then, species by species again, M_s =
+// (dE/dA h_s) W3^T and the backward tiles of (s, i).  The activation stash is
+// shared by a receiver's units (its first STASH_TILES tiles in s order).  With
+// C = 64, W3 sits in LDS too (read along rows for A, down columns for M);
+// with C = 128 it is read from global memory (W3 and its transposed copy).
+constexpr int MULTI_MAX_S = 3;
+
+template <int C, bool W3L>
+struct MultiLds {
+  static constexpr int PW = FoldLds<C>::BWD_ONLY > FoldLds<C>::FWD_ONLY ? FoldLds<C>::BWD_ONLY : FoldLds<C>::FWD_ONLY;
+  static constexpr int WEIGHTS = W3L ? Lds<C>::FLOATS : W12_FLOATS;
+};
+
+template <int C, int W, bool W3L>
+__global__ void __launch_bounds__(64 * W)
+k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t* __restrict__ zstart,
+             const float* __restrict__ W1, const float* __restrict__ W2, const float* __restrict__ W3,
+             const float* __restrict__ W3T, const float* __restrict__ emb, const float* __restrict__ w_read,
+             float* __restrict__ ei, float* __restrict__ gout, float* __restrict__ stash) {
+  constexpr int NC = 4 * C, CPL = C / 64;
+  __shared__ float wl[MultiLds<C, W3L>::WEIGHTS];
+  __shared__ __align__(16) float wbuf[W][MultiLds<C, W3L>::PW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const WaveLds<C> L(wbuf[wave]);
+  const float* w1s = wl + Lds<C>::W1;
+  const float* w2s = wl + Lds<C>::W2;
+  const int N = un.n_atoms, S = un.S;
+  // batches of W receivers of one species, species after species
+  int bstart[MULTI_MAX_S + 1];
+  bstart[0] = 0;
+#pragma unroll
+  for (int z = 0; z < MULTI_MAX_S; ++z)
+    bstart[z + 1] = bstart[z] + (z < S ? (zstart[z + 1] - zstart[z] + W - 1) / W : 0);
+  const int total = bstart[MULTI_MAX_S];
+  float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+  auto stage = [&](int p) {
+    __syncthreads();
+    if (W3L)
+      stage_weights<C>(wl, W1, W2, W3, p);
+    else
+      stage_w12(wl, W1, W2, p);
+    __syncthreads();
+  };
+  for (int b = blockIdx.x; b < total; b += gridDim.x) {
+    int z = 0;
+#pragma unroll
+    for (int k = 1; k < MULTI_MAX_S; ++k) z += (k < S && bstart[k] <= b) ? 1 : 0;
+    const int zb = z == 0 ? 0 : (z == 1 ? bstart[1] : bstart[2]);
+    const int idx = zstart[z] + (b - zb) * W + wave;
+    const bool valid = idx < zstart[z + 1];
+    const int i = valid ? min(max(ord[idx], 0), N - 1) : 0;
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const Recv xi = recv_pos(in, i);
+    float acc[CPL][NLM];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) acc[q][k] = 0.f;
+    int t = 0;
+    for (int sp = 0; sp < S; ++sp) {
+      const int p = z * S + sp;
+      stage(p);
+      const int qa = valid ? un.seg[2 * ((size_t)sp * N + i)] : 0;
+      const int qb = valid ? un.seg[2 * ((size_t)sp * N + i) + 1] : 0;
+      if (qb <= qa) continue;
+      f32x4 T[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) T[bb] = zero4();
+      for (int q0 = qa; q0 < qb; q0 += 32, ++t)
+        fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
+                 t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr);
+      float as[CPL][NLM];
+      if (W3L)
+        unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, as);
+      else
+        unit_last_layer<C, NC>(T, L.tsm, W3 + (size_t)p * HID * NC, lane, as);
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const float hc = emb[(size_t)sp * C + lane + 64 * q];
+#pragma unroll
+        for (int k = 0; k < NLM; ++k) acc[q][k] += hc * as[q][k];
+      }
+    }
+    // E_i = sum_c w_c sum_lm A^2; acc becomes dE/dA = 2 w A
+    float esum = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const float wc = w_read[lane + 64 * q];
+      float sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < NLM; ++k) {
+        sq += acc[q][k] * acc[q][k];
+        acc[q][k] *= 2.f * wc;
+      }
+      esum += wc * sq;
+    }
+    for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
+    if (valid && lane == 0) ei[i] = esum;
+    t = 0;
+    for (int sp = 0; sp < S; ++sp) {
+      const int p = z * S + sp;
+      stage(p);
+      const int qa = valid ? un.seg[2 * ((size_t)sp * N + i)] : 0;
+      const int qb = valid ? un.seg[2 * ((size_t)sp * N + i) + 1] : 0;
+      if (qb <= qa) continue;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c = lane + 64 * q;
+        const float hc = emb[(size_t)sp * C + c];
+#pragma unroll
+        for (int k = 0; k < NLM; ++k) L.ahsm[c][k] = acc[q][k] * hc;
+      }
+      wave_sync_lds();
+      if (W3L)
+        unit_M<C, 1>(L.ahsm, wl + Lds<C>::W3 + lane * Lds<C>::LD3, lane, L.msm);
+      else
+        unit_M<C, HID>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
+      for (int q0 = qa; q0 < qb; q0 += 32, ++t)
+        bwd_tile(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout,
+                 t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr);
+    }
+  }
+}
+
 // W3T[p][j][k] = W3[p][k][j]: the backward reads W3 down its columns.
 __global__ void k_transpose_w3(int P, int NC, const float* __restrict__ W3, float* __restrict__ W3T) {
   const int64_t n = (int64_t)P * HID * NC;
@@ -727,12 +857,37 @@ constexpr int SPLIT_MAX_ATOMS = 768;  // past it a wave per receiver is faster (
 bool use_split(const ConvPlan& p) { return p.N <= SPLIT_MAX_ATOMS; }
 int split_grid(const ConvPlan& p) { return std::max(1, std::min(p.N, 256)); }
 
+int multi_grid(const ConvPlan& p) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>((p.N + WAVES - 1) / WAVES + p.S, 256));
+}
+
 }  // namespace
 
+bool fold_multi_supported(const ConvPlan& p) { return p.S >= 2 && p.S <= MULTI_MAX_S; }
+
 size_t fold_stash_bytes(const ConvPlan& p) {
-  if (p.S != 1) return 0;
-  const int waves = use_split(p) ? split_grid(p) * WAVES : unit_grid(p) * WAVES;
+  int waves = 0;
+  if (p.S == 1) waves = (use_split(p) ? split_grid(p) : unit_grid(p)) * WAVES;
+  else if (fold_multi_supported(p)) waves = multi_grid(p) * WAVES;
   return sizeof(float) * (size_t)waves * STASH_TILES * 32 * ZROW;
+}
+
+void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
+                       char* ws) {
+  if (p.N == 0) return;
+  const float* W3T = (const float*)(ws + p.off_w3t);
+  float* stash = (float*)(ws + p.off_stash);
+  const int32_t* ord = (const int32_t*)(ws + p.off_ord);
+  const int32_t* zstart = (const int32_t*)(ws + p.off_zstart);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
+  const Units un = make_units(p, g, species, ws);
+  if (p.C == 64)
+    k_fold_multi<64, WAVES, true><<<multi_grid(p), 64 * WAVES, 0, s>>>(in, un, ord, zstart, m->W1, m->W2, m->W3,
+                                                                        W3T, m->emb, m->w_read, ei, gout, stash);
+  else
+    k_fold_multi<128, WAVES, false><<<multi_grid(p), 64 * WAVES, 0, s>>>(in, un, ord, zstart, m->W1, m->W2, m->W3,
+                                                                          W3T, m->emb, m->w_read, ei, gout, stash);
 }
 
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,
