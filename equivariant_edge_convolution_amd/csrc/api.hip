@@ -286,8 +286,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   if (folded && fold_multi_supported(p)) {
     // one kernel per call from geometry to dE/dd, sender species after species
     mark(2 * EEC_PHASE_PREPARE);
-    launch_prepare(s, p, g, species, ws, nullptr);
-    launch_species_order(s, p, species, ws);
+    launch_prepare_rows(s, p, g, species, ws);
     launch_transpose_w3(s, p, m, ws);
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);

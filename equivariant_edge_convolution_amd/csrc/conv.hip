@@ -163,6 +163,50 @@ __global__ void __launch_bounds__(256) k_seg_bounds(int32_t n, int S, const int3
   seg[2 * t + 1] = (int32_t)lo2;
 }
 
+// Row-local grouping by sender species: perm lists row i's edges with the
+// senders of species 0 first, then 1, ..., each group in CSR order, and
+// seg[s][i] is the position range of group s (positions are CSR positions).
+// One wave per row: a counting pass, then a placing pass, by ballots.
+__global__ void __launch_bounds__(256) k_row_partition(int32_t n, int S, int64_t E, const int32_t* __restrict__ rp,
+                                                       const int32_t* __restrict__ col,
+                                                       const int32_t* __restrict__ species,
+                                                       int32_t* __restrict__ perm, int32_t* __restrict__ seg) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int i = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < n; i += (int)((gridDim.x * blockDim.x) >> 6)) {
+    const int a = max(0, min(rp[i], (int)E)), b = max(a, min(rp[i + 1], (int)E));
+    int cnt[4] = {0, 0, 0, 0};
+    for (int e0 = a; e0 < b; e0 += 64) {
+      const int e = e0 + lane;
+      const int sp = e < b ? min(max(species[min(max(col[e], 0), n - 1)], 0), S - 1) : -1;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) cnt[z] += __popcll(__ballot(sp == z));
+    }
+    int start[4];
+    start[0] = a;
+#pragma unroll
+    for (int z = 1; z < 4; ++z) start[z] = start[z - 1] + cnt[z - 1];
+    if (lane < S) {
+      int lo = start[0], hi = start[0] + cnt[0];
+#pragma unroll
+      for (int z = 1; z < 4; ++z)
+        if (lane == z) { lo = start[z]; hi = start[z] + cnt[z]; }
+      seg[2 * ((size_t)lane * n + i)] = lo;
+      seg[2 * ((size_t)lane * n + i) + 1] = hi;
+    }
+    for (int e0 = a; e0 < b; e0 += 64) {
+      const int e = e0 + lane;
+      const int sp = e < b ? min(max(species[min(max(col[e], 0), n - 1)], 0), S - 1) : -1;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const uint64_t m = __ballot(sp == z);
+        if (sp == z) perm[start[z] + __popcll(m & below)] = e;
+        start[z] += __popcll(m);
+      }
+    }
+  }
+}
+
 // Atoms ordered by species, stably, and the species' offsets in that order
 // (zstart [S+1]): one workgroup, each thread a contiguous slice of atoms.
 constexpr int SO_T = 1024;
@@ -525,8 +569,10 @@ void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
   }
 }
 
-void launch_species_order(hipStream_t s, const ConvPlan& p, const int32_t* species, char* ws) {
+void launch_prepare_rows(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species, char* ws) {
   if (p.S > 4 || p.S < 2 || p.N == 0) return;
+  k_row_partition<<<blocks_for(p.N, 4), 256, 0, s>>>(p.N, p.S, p.E, g->row_ptr, g->col, species,
+                                                     (int32_t*)(ws + p.off_perm), (int32_t*)(ws + p.off_seg));
   k_species_order<<<1, SO_T, 0, s>>>(p.N, p.S, species, (int32_t*)(ws + p.off_ord), (int32_t*)(ws + p.off_zstart));
 }
 

@@ -53,8 +53,10 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
 void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
                     char* ws, float* zero_rows_of /* [N][16][C] or NULL */);
 
-// Atoms in species order (stable) and the species' offsets, for 2 <= S <= 4.
-void launch_species_order(hipStream_t s, const ConvPlan& p, const int32_t* species, char* ws);
+// For 2 <= S <= 4: row-local grouping of the edges by sender species (perm and
+// seg in the layout launch_prepare uses, positions being CSR positions), and
+// the atoms in species order (stable) with the species' offsets.
+void launch_prepare_rows(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species, char* ws);
 
 // Radial network over a range of edges.  When `basis_in` is given the basis is
 // read from it (materialising entry point); otherwise it is computed from the
