@@ -89,20 +89,34 @@ __device__ __forceinline__ void sched_init(const Sched& sc, SchedState& st) {
   __syncthreads();
 }
 
+// A row-major [rows][cols] global matrix (cols a multiple of 4) into LDS with
+// row stride ld, by the whole workgroup: 16-byte loads when the source allows.
+__device__ __forceinline__ void stage_rows(float* lds, int ld, const float* __restrict__ g, int rows, int cols) {
+  if ((reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const int n4 = rows * cols / 4;
+    for (int k = threadIdx.x; k < n4; k += blockDim.x) {
+      const float4 v = g4[k];
+      float* d = lds + ((4 * k) / cols) * ld + (4 * k) % cols;
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+  } else {
+    for (int k = threadIdx.x; k < rows * cols; k += blockDim.x) lds[(k / cols) * ld + k % cols] = g[k];
+  }
+}
+
 template <int C>
 __device__ __forceinline__ void stage_weights(float* lds, const float* __restrict__ W1, const float* __restrict__ W2,
                               const float* __restrict__ W3, int p) {
   constexpr int NC = Lds<C>::NC;
-  const float* w1 = W1 + (size_t)p * NB * HID;
-  const float* w2 = W2 + (size_t)p * HID * HID;
-  const float* w3 = W3 + (size_t)p * HID * NC;
-  for (int k = threadIdx.x; k < NB * HID; k += blockDim.x)
-    lds[Lds<C>::W1 + (k / HID) * LDH + k % HID] = w1[k];
-  for (int k = threadIdx.x; k < HID * HID; k += blockDim.x)
-    lds[Lds<C>::W2 + (k / HID) * LDH + k % HID] = w2[k];
-  for (int k = threadIdx.x; k < HID * NC; k += blockDim.x)
-    lds[Lds<C>::W3 + (k / NC) * Lds<C>::LD3 + k % NC] = w3[k];
+  stage_rows(lds + Lds<C>::W1, LDH, W1 + (size_t)p * NB * HID, NB, HID);
+  stage_rows(lds + Lds<C>::W2, LDH, W2 + (size_t)p * HID * HID, HID, HID);
+  stage_rows(lds + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
 }
+
 
 // Schedule of a run of NMFMA matrix instructions whose B operands come from
 // LDS (one read per PER instructions): PRE reads are issued ahead and each group
@@ -261,11 +275,8 @@ struct Units {
 constexpr int W12_FLOATS = NB * LDH + HID * LDH;
 __device__ __forceinline__ void stage_w12(float* lds, const float* __restrict__ W1,
                                           const float* __restrict__ W2, int p) {
-  const float* w1 = W1 + (size_t)p * NB * HID;
-  const float* w2 = W2 + (size_t)p * HID * HID;
-  for (int k = threadIdx.x; k < NB * HID; k += blockDim.x) lds[(k / HID) * LDH + k % HID] = w1[k];
-  for (int k = threadIdx.x; k < HID * HID; k += blockDim.x)
-    lds[NB * LDH + (k / HID) * LDH + k % HID] = w2[k];
+  stage_rows(lds, LDH, W1 + (size_t)p * NB * HID, NB, HID);
+  stage_rows(lds + NB * LDH, LDH, W2 + (size_t)p * HID * HID, HID, HID);
 }
 
 // Position range [qa, qb) of unit (p, i) in the pair-grouped order; false when

@@ -682,7 +682,8 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
 // s in turn the workgroup stages the weights of pair (Z_i, s) in LDS and every
 // wave runs the forward tiles of its unit (s, i) and adds h_s T_s^T W3 to its
 // A; then E_i and dE/dA; then, species by species again, M_s =
-// (dE/dA h_s) W3^T and the backward tiles of (s, i).  The activation stash is
+// (dE/dA h_s) W3^T and the backward tiles of (s, i), in reverse order so that
+// the last forward species' weights are reused.  The activation stash is
 // shared by a receiver's units (its first STASH_TILES tiles in s order).  With
 // C = 64, W3 sits in LDS too (read along rows for A, down columns for M);
 // with C = 128 it is read from global memory (W3 and its transposed copy).
@@ -780,13 +781,18 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
     }
     for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
     if (valid && lane == 0) ei[i] = esum;
-    t = 0;
-    for (int sp = 0; sp < S; ++sp) {
+    // backward in reverse species order: the last forward species' weights are
+    // still staged
+    for (int r = 0; r < S; ++r) {
+      const int sp = S - 1 - r;
       const int p = z * S + sp;
-      stage(p);
+      if (r > 0) stage(p);
       const int qa = valid ? un.seg[2 * ((size_t)sp * N + i)] : 0;
       const int qb = valid ? un.seg[2 * ((size_t)sp * N + i) + 1] : 0;
       if (qb <= qa) continue;
+      int t = 0;  // the forward's tile count before species sp
+      for (int s2 = 0; s2 < sp; ++s2)
+        t += (un.seg[2 * ((size_t)s2 * N + i) + 1] - un.seg[2 * ((size_t)s2 * N + i)] + 31) >> 5;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         const int c = lane + 64 * q;
