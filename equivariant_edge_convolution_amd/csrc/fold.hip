@@ -543,17 +543,22 @@ __device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane
 constexpr int LDG = HID + 1;                       // row stride of G_l in LDS
 constexpr int GRAM_FLOATS = 4 * HID * LDG;
 
-// G_l[k][k'] for one species pair: block (l, k), thread k'; binary64 sums.
-__global__ void __launch_bounds__(64) k_gram(int C, const float* __restrict__ W3, const float* __restrict__ emb,
-                                             const float* __restrict__ w_read, float* __restrict__ G) {
-  const int l = blockIdx.x >> 6, k = blockIdx.x & 63, kk = threadIdx.x;
-  const float* a = W3 + (size_t)k * 4 * C + l * C;
-  const float* b = W3 + (size_t)kk * 4 * C + l * C;
+// G_l[k][k'] for one species pair.  Block (l, four rows k): the degree-l
+// columns of W3 (64 x C) in LDS, one entry per thread, binary64 sums over c.
+constexpr int GRAM_T = 256;
+constexpr int GRAM_BLOCKS = 4 * HID * HID / GRAM_T;
+__global__ void __launch_bounds__(GRAM_T) k_gram(int C, const float* __restrict__ W3, const float* __restrict__ emb,
+                                                 const float* __restrict__ w_read, float* __restrict__ G) {
+  __shared__ float w3l[HID][128 + 1];  // [k][c], C <= 128
+  __shared__ double d[128];           // 2 w_c h_c^2
+  constexpr int ROWS = GRAM_T / HID;
+  const int l = blockIdx.x / (HID / ROWS), k0 = ROWS * (blockIdx.x % (HID / ROWS));
+  for (int t = threadIdx.x; t < HID * C; t += GRAM_T) w3l[t / C][t % C] = W3[(size_t)(t / C) * 4 * C + l * C + t % C];
+  for (int c = threadIdx.x; c < C; c += GRAM_T) d[c] = 2.0 * (double)w_read[c] * (double)emb[c] * (double)emb[c];
+  __syncthreads();
+  const int k = k0 + threadIdx.x / HID, kk = threadIdx.x % HID;
   double acc = 0.0;
-  for (int c = 0; c < C; ++c) {
-    const double hc = emb[c];
-    acc += 2.0 * (double)w_read[c] * hc * hc * (double)a[c] * (double)b[c];
-  }
+  for (int c = 0; c < C; ++c) acc += d[c] * (double)w3l[k][c] * (double)w3l[kk][c];
   G[((size_t)l * HID + k) * HID + kk] = (float)acc;
 }
 
@@ -917,7 +922,7 @@ void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, c
 bool fold_fused_supported(const ConvPlan& p) { return p.S == 1; }
 
 void launch_gram(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws) {
-  k_gram<<<4 * HID, HID, 0, s>>>(p.C, m->W3, m->emb, m->w_read, (float*)(ws + p.off_w3t));
+  k_gram<<<GRAM_BLOCKS, GRAM_T, 0, s>>>(p.C, m->W3, m->emb, m->w_read, (float*)(ws + p.off_w3t));
 }
 
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,

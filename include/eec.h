@@ -211,8 +211,9 @@ EEC_API eec_status eec_energy_forces(void *stream, const eec_graph *g, const dou
  *             A_i[lm][c] = sum_s h_{s,c} sum_k T_{i,s}[k][lm] W3_{(Z_i,s)}[k][l C + c];
  *   backward: M_{i,s}[lm][k] = sum_c (dE/dA_i)[lm][c] h_{s,c} W3_{(Z_i,s)}[k][l C + c],
  *             dE/dY_e = M s2_e,  dE/ds2_e = M^T Y_e.
- * The per-edge radial weights R are never formed.  With one species the
- * whole call per receiver runs in one kernel, and the quadratic readout is
+ * The per-edge radial weights R are never formed.  With one to three species
+ * the whole call per receiver (forward, readout, backward) runs in one
+ * kernel; with one species the quadratic readout is
  * taken through per-degree Gram matrices
  *   G_l[k][k'] = sum_c 2 w_c h_c^2 W3[k][lC+c] W3[k'][lC+c]:
  *   M_i[lm] = G_l(lm) T_i[lm],  E_i = 1/2 sum_lm T_i[lm] . M_i[lm],
@@ -231,15 +232,17 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * each phase: events[2k] before and events[2k+1] after phase k, for
  *   k = EEC_PHASE_PREPARE   receiver index and pair grouping, and for the
  *                           folded variant the transpose of W3 (folded, one
- *                           species: that transpose for C != 64 only),
+ *                           species: the Gram matrices instead; two or three
+ *                           species: the grouping of each row by sender
+ *                           species and the atoms in species order),
  *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
  *                           radial-row chunks and message passes; folded,
- *                           one species: the single fused kernel launch,
- *                           forward and backward),
- *       EEC_PHASE_READOUT   per-atom energies and dE/dA (folded, one
- *                           species: empty),
+ *                           one to three species: the single fused kernel
+ *                           launch, forward, readout and backward),
+ *       EEC_PHASE_READOUT   per-atom energies and dE/dA (folded, one to
+ *                           three species: empty),
  *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch;
- *                           folded, one species: empty),
+ *                           folded, one to three species: empty),
  *       EEC_PHASE_SCATTER   forces and the energy total in one kernel launch
  *                           (with the virial, a second launch totals both).
  * `events` holds 2 * EEC_N_PHASES handles (a NULL entry skips that record);
