@@ -180,6 +180,137 @@ def message_mode(args, B, torch, cfg, g, pos, species, model, dev) -> int:
     return 0
 
 
+def md_loop(B, torch, cfg, model, dev, steps: int, skin: float, scheme: str, variant: str = "folded",
+            warmup: int = 0, record: bool = False) -> dict:
+    """An MD-like loop over the synthetic trajectory of eec_inputs (atoms on
+    seeded straight lines and back): per step one energy/force call, with the
+    neighbour list kept by one of three schemes
+      "every"   rebuilt at the model cutoff before every call;
+      "serial"  built with cutoff rc + skin and reused; when the skin test
+                (eec_skin_check) of the previous step found an atom past the
+                trigger, rebuilt on the call's stream after the step's call;
+      "side"    the same decisions, the rebuild on a second stream beside the
+                step's call, the next call waiting for it (an event).
+    The skin test of step t is read by the host at step t + 1 (it ran before
+    the call of step t), so the loop never drains the stream for it; to keep
+    every list valid with that lag the trigger is skin / 2 - 2 max_i |v_i|
+    (v_i the per-step motion).  Positions stay in the frame of the list they
+    are used with (wrapped into the cell at each rebuild only).  The last
+    `steps` of warmup + steps are timed; with `record`, each step's energy,
+    forces and largest squared displacement are returned too."""
+    import numpy as np
+
+    import eec_inputs as I
+
+    rc, n, S = cfg.model.cutoff, cfg.n_atoms, cfg.model.n_species
+    species = torch.as_tensor(cfg.species).to(dev)
+    x0 = torch.as_tensor(cfg.pos).to(dev)
+    vel_np = I.md_velocities(n)
+    vel = torch.as_tensor(vel_np).to(dev)
+    Lt = torch.as_tensor(np.asarray(cfg.box, np.float64)).to(dev)
+    vmax = float(np.sqrt((vel_np * vel_np).sum(axis=1)).max())
+    every = scheme == "every"
+    lc = rc if every else rc + skin
+    trig = 0.5 * skin - 2.0 * vmax
+    if not every and trig <= 0.0:
+        raise ValueError(f"skin {skin} too small for a per-step motion of up to {vmax:.4f} A")
+
+    def u(t):
+        return x0 + vel * I.md_phase(t)
+
+    def wrapped(x):
+        w = torch.remainder(x, Lt)
+        return torch.where(w >= Lt, w - Lt, w)
+
+    g0 = B.build_neighbors(x0, cfg.box, lc, species, S)
+    cap = int(1.25 * g0.n_edges) + 1024
+    lists = [B.NeighborList(n, cfg.box, lc, cap, dev, species, S) for _ in range(2)]
+    ef = B.EnergyForces(g0, model, dev, atom_energy=False, variant=variant, edge_capacity=cap)
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev) if scheme == "side" else None
+    total = warmup + steps
+    m2 = torch.zeros(total, dtype=torch.float64, device=dev)
+    flag = torch.zeros(total, dtype=torch.int32, device=dev)
+    flag_h = torch.zeros(total, dtype=torch.int32, pin_memory=True)
+    checked = [None] * total
+    rec_E, rec_F = [], []
+    ref = x0
+    off = torch.zeros_like(x0)
+    cur, nxt = lists[0].build(x0), 1
+    valid_from, rebuilds, edges = 0, 0, 0
+    t0 = None
+    for t in range(total):
+        if t == warmup:
+            torch.cuda.synchronize()
+            t0, rebuilds, edges = time.perf_counter(), 0, 0
+        ut = u(t)
+        if every:
+            pos_t = wrapped(ut)
+            cur = lists[nxt].build(pos_t)
+            nxt ^= 1
+            rebuilds += 1
+        else:
+            pos_t = ut - off
+            B.skin_check(pos_t, ref, trig, out=(m2[t:t + 1], flag[t:t + 1]))
+            flag_h[t:t + 1].copy_(flag[t:t + 1], non_blocking=True)
+            checked[t] = torch.cuda.Event()
+            checked[t].record(main)
+        rebuild = False
+        if not every and t - 1 >= valid_from:
+            checked[t - 1].synchronize()
+            rebuild = bool(flag_h[t - 1])
+        if rebuild:
+            w = wrapped(ut)
+            if side is not None:
+                ready = torch.cuda.Event()
+                ready.record(main)
+        ef(pos_t, cfg.box, species, graph=cur)
+        edges += cur.n_edges
+        if record:
+            rec_E.append(ef.energy.clone())
+            rec_F.append(ef.forces.clone())
+        if rebuild:
+            if side is not None:
+                with torch.cuda.stream(side):
+                    side.wait_event(ready)
+                    cur = lists[nxt].build(w)
+                    built = torch.cuda.Event()
+                    built.record(side)
+                main.wait_event(built)
+            else:
+                cur = lists[nxt].build(w)
+            nxt ^= 1
+            ref, off = w, ut - w
+            valid_from = t + 1
+            rebuilds += 1
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    out = {"scheme": scheme, "skin": 0.0 if every else skin, "list_cutoff": lc, "ms_per_step": dt * 1e3 / steps,
+           "rebuilds": rebuilds, "mean_edges": edges / steps, "trigger": None if every else trig,
+           "max_step_motion": vmax}
+    if record:
+        out["E"] = [float(e.cpu()[0]) for e in rec_E]
+        out["F"] = [f.cpu().numpy() for f in rec_F]
+        out["max_r2"] = m2.cpu().numpy()
+    return out
+
+
+def md_mode(args, B, torch, cfg, model, dev) -> int:
+    """Time the MD-like loop (md_loop) under its three list schemes."""
+    res = {}
+    for scheme in ("every", "serial", "side"):
+        r = md_loop(B, torch, cfg, model, dev, args.steps, args.skin, scheme, args.variant, warmup=args.warmup)
+        res[scheme] = r
+        print(json.dumps({"mode": "md", "config": args.config, **r}), flush=True)
+    call = res["serial"]
+    print(json.dumps({"mode": "md_summary", "config": args.config, "variant": args.variant,
+                      "skin": args.skin, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": {k: v["ms_per_step"] for k, v in res.items()},
+                      "steps_per_rebuild": args.steps / max(call["rebuilds"], 1),
+                      "side_over_serial": res["side"]["ms_per_step"] / call["ms_per_step"]}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,10 +324,13 @@ def main() -> int:
     ap.add_argument("--variant", default="folded", choices=["direct", "folded"],
                     help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
                          "last radial layer moved past the edge sum (eec_energy_forces_folded)")
-    ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy"],
+    ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy", "md"],
                     help="energy_forces: the headline call; edge_message: the chunked streaming "
                          "forward (radial rows + message pass), for profiling its kernels; copy: a "
-                         "plain 256 MiB device copy, the calibration of the HBM byte counters")
+                         "plain 256 MiB device copy, the calibration of the HBM byte counters; md: an "
+                         "MD-like loop with a Verlet-skin neighbour list, rebuilt serially or on a "
+                         "side stream, against a rebuild before every call")
+    ap.add_argument("--skin", type=float, default=0.2, help="Verlet skin of --mode md, A")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -213,6 +347,8 @@ def main() -> int:
     if args.mode == "copy":
         return copy_calibration(args, torch, dev)
     cfg = I.make_config(args.config)
+    if args.mode == "md":
+        return md_mode(args, B, torch, cfg, B.Model.from_arrays(cfg.model, dev), dev)
     pos = torch.as_tensor(cfg.pos).to(dev)
     species = torch.as_tensor(cfg.species).to(dev)
     model = B.Model.from_arrays(cfg.model, dev)

@@ -172,3 +172,28 @@ def random_rotation(seed: int) -> np.ndarray:
     if np.linalg.det(q) < 0:
         q[:, 0] = -q[:, 0]
     return q
+
+
+# ---------------------------------------------------------------- MD motion
+# A synthetic trajectory for exercising a Verlet-skin neighbour list: every
+# atom moves along its own seeded straight line and back, its offset from the
+# start following a triangle wave (amplitude period / 4 steps of its
+# velocity), so the structure stays close to the lattice for any number of
+# steps while the list still has to be rebuilt every few steps.
+MD_SIGMA = 0.003  # A per step, per component
+MD_PERIOD = 40  # steps
+
+
+def md_velocities(n_atoms: int, seed: int = 0, sigma: float = MD_SIGMA) -> np.ndarray:
+    return np.random.default_rng(np.random.SeedSequence(seed).spawn(5)[4]).normal(0.0, sigma, (n_atoms, 3))
+
+
+def md_phase(step: int, period: int = MD_PERIOD) -> float:
+    """Triangle wave: 0 at step 0, slope +1 then -1, extremes +-period / 4."""
+    q = period / 4.0
+    return q - abs(((step + q) % period) - 2.0 * q)
+
+
+def md_positions(pos0: np.ndarray, vel: np.ndarray, step: int, period: int = MD_PERIOD) -> np.ndarray:
+    """Unwrapped positions at `step` (the frame of pos0; not mapped into the cell)."""
+    return pos0 + vel * md_phase(step, period)

@@ -30,7 +30,7 @@ EEC_ERR_CAPACITY = 6
 
 # every entry point include/eec.h declares
 SYMBOLS = (
-    "eec_build_neighbors", "eec_neighbors_workspace_bytes", "eec_radial_basis",
+    "eec_build_neighbors", "eec_neighbors_workspace_bytes", "eec_skin_check", "eec_radial_basis",
     "eec_radial_project", "eec_project_workspace_bytes", "eec_edge_message",
     "eec_energy_forces", "eec_energy_forces_folded", "eec_energy_forces_timed", "eec_workspace_bytes",
     "eec_last_error",
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.eec_neighbors_workspace_bytes.argtypes = [i32, P(dbl), dbl]
     L.eec_build_neighbors.restype = ctypes.c_int
     L.eec_build_neighbors.argtypes = [vp, i32, vp, P(dbl), dbl, vp, i32, i64, vp, vp, vp, vp, P(i64), vp, sz]
+    L.eec_skin_check.restype = ctypes.c_int
+    L.eec_skin_check.argtypes = [vp, i32, vp, vp, dbl, vp, vp]
     L.eec_radial_basis.restype = ctypes.c_int
     L.eec_radial_basis.argtypes = [vp, P(_Graph), vp, P(dbl), dbl, vp, vp, vp]
     L.eec_project_workspace_bytes.restype = sz
@@ -213,6 +215,46 @@ def build_neighbors(pos: torch.Tensor, box, cutoff: float, species: torch.Tensor
     raise EECError(EEC_ERR_CAPACITY, "build_neighbors", "capacity retry failed")
 
 
+class NeighborList:
+    """Preallocated CSR buffers (``edge_capacity`` edges) and workspace for
+    repeated eec_build_neighbors calls on one cell, e.g. the rebuilds of an MD
+    loop, which may run on a side stream (the current stream at ``build``)."""
+
+    def __init__(self, n_atoms: int, box, cutoff: float, edge_capacity: int, device,
+                 species: torch.Tensor | None = None, n_species: int = 0):
+        self.n, self.box, self.cutoff = int(n_atoms), box, float(cutoff)
+        self.cap = int(edge_capacity)
+        self.species, self.n_species = species, int(n_species)
+        self.row_ptr = torch.empty(self.n + 1, dtype=torch.int32, device=device)
+        self.col = torch.empty(max(self.cap, 1), dtype=torch.int32, device=device)
+        self.shift = torch.empty((max(self.cap, 1), 3), dtype=torch.int8, device=device)
+        self.rev = torch.empty(max(self.cap, 1), dtype=torch.int32, device=device)
+        self.workspace = _workspace(neighbors_workspace_bytes(self.n, box, cutoff), device)
+
+    def build(self, pos: torch.Tensor) -> Graph:
+        """Build into the buffers on the current stream; returns a Graph view
+        of them (its arrays are complete once that stream reaches this point)."""
+        ne = ctypes.c_int64(0)
+        st = lib().eec_build_neighbors(_stream(pos.device), self.n, _ptr(pos), _box(self.box), self.cutoff,
+                                       _ptr(self.species), self.n_species, self.cap, _ptr(self.row_ptr),
+                                       _ptr(self.col), _ptr(self.shift), _ptr(self.rev), ctypes.byref(ne),
+                                       _ptr(self.workspace), self.workspace.numel())
+        _check(st, "build_neighbors")
+        E = int(ne.value)
+        return Graph(self.n, E, self.row_ptr, self.col[:E], self.shift[:E], self.rev[:E])
+
+
+def skin_check(pos: torch.Tensor, ref: torch.Tensor, half_skin: float, out=None):
+    """eec_skin_check on the current stream: (max_r2 [1] float64, rebuild [1]
+    int32), device tensors, nothing synchronised."""
+    dev = pos.device
+    m2, flag = out if out is not None else (torch.empty(1, dtype=torch.float64, device=dev),
+                                            torch.empty(1, dtype=torch.int32, device=dev))
+    _check(lib().eec_skin_check(_stream(dev), int(pos.shape[0]), _ptr(pos), _ptr(ref), float(half_skin),
+                                _ptr(m2), _ptr(flag)), "skin_check")
+    return m2, flag
+
+
 def radial_basis(graph: Graph, pos: torch.Tensor, box, cutoff: float):
     dev = pos.device
     E = graph.n_edges
@@ -252,7 +294,7 @@ class EnergyForces:
     """Preallocated outputs + workspace for repeated eec_energy_forces calls."""
 
     def __init__(self, graph: Graph, model: Model, device, atom_energy=True, virial=False,
-                 variant: str = "direct"):
+                 variant: str = "direct", edge_capacity: int | None = None):
         n = graph.n_atoms
         self.variant = VARIANTS[variant]
         self.graph, self.model = graph, model
@@ -260,14 +302,20 @@ class EnergyForces:
         self.atom_energy = torch.empty(n, dtype=torch.float32, device=device) if atom_energy else None
         self.forces = torch.empty((n, 3), dtype=torch.float32, device=device)
         self.virial = torch.empty((3, 3), dtype=torch.float32, device=device) if virial else None
-        self.workspace = _workspace(workspace_bytes(n, graph.n_edges, model), device)
+        self.cap = max(graph.n_edges, 0 if edge_capacity is None else int(edge_capacity))
+        self.workspace = _workspace(workspace_bytes(n, self.cap, model), device)
         self._g = graph.struct()
         self._m = model.struct()
 
-    def __call__(self, pos: torch.Tensor, box, species: torch.Tensor, events=None):
+    def __call__(self, pos: torch.Tensor, box, species: torch.Tensor, events=None, graph: Graph | None = None):
         """One eec_energy_forces call on the current stream; with ``events`` (a
         sequence of 2 * len(PHASES) hipEvent_t handles) the instrumented entry
-        point records them around each phase."""
+        point records them around each phase.  ``graph`` replaces the bound
+        list (same atoms, at most ``edge_capacity`` edges), e.g. after a rebuild."""
+        if graph is not None:
+            if graph.n_atoms != self.graph.n_atoms or graph.n_edges > self.cap:
+                raise ValueError("graph does not fit this EnergyForces (atoms or edge capacity)")
+            self.graph, self._g = graph, graph.struct()
         s = _stream(pos.device)
         args = (s, ctypes.byref(self._g), _ptr(pos), _box(box), _ptr(species), ctypes.byref(self._m),
                 _ptr(self.energy), _ptr(self.atom_energy), _ptr(self.forces), _ptr(self.virial),

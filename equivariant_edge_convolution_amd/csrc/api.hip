@@ -150,6 +150,20 @@ eec_status eec_build_neighbors(void* stream, int32_t n_atoms, const double* pos,
   return launched("build_neighbors");
 }
 
+eec_status eec_skin_check(void* stream, int32_t n_atoms, const double* pos, const double* ref,
+                          double half_skin, double* max_r2, int32_t* rebuild) {
+  if (max_r2 == nullptr || rebuild == nullptr) return fail(EEC_ERR_NULL, "max_r2 or rebuild is NULL");
+  if (n_atoms < 0) return fail(EEC_ERR_SHAPE, "negative size");
+  if (n_atoms > 0 && (pos == nullptr || ref == nullptr)) return fail(EEC_ERR_NULL, "pos or ref is NULL");
+  if (!(isfinite(half_skin) && half_skin >= 0.0)) return fail(EEC_ERR_SHAPE, "half_skin must be finite and >= 0");
+  if (((uintptr_t)max_r2 & 7) != 0 || ((uintptr_t)rebuild & 3) != 0)
+    return fail(EEC_ERR_SHAPE, "max_r2 must be 8-byte and rebuild 4-byte aligned");
+  TRY(check_alias({span(max_r2, 8, "max_r2"), span(rebuild, 4, "rebuild")},
+                  {span(pos, 24 * (size_t)n_atoms, "pos"), span(ref, 24 * (size_t)n_atoms, "ref")}));
+  launch_skin_check((hipStream_t)stream, n_atoms, pos, ref, half_skin, max_r2, rebuild);
+  return launched("skin_check");
+}
+
 eec_status eec_radial_basis(void* stream, const eec_graph* g, const double* pos, const double* box,
                             double cutoff, float* r, float* basis, float* Y) {
   TRY(check_graph(g));

@@ -36,6 +36,11 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n_atoms, const doubl
                     int64_t cap, int32_t* row_ptr, int32_t* col, int8_t* shift, int32_t* rev,
                     int64_t* n_edges, char* ws, const char** why);
 
+// Skin test: *max_r2 = largest squared displacement pos - ref over the atoms,
+// *rebuild = (*max_r2 > half_skin^2); both written on the stream, no sync.
+void launch_skin_check(hipStream_t s, int32_t n, const double* pos, const double* ref, double half_skin,
+                       double* max_r2, int32_t* rebuild);
+
 // ---- edge-convolution workspace plan
 struct ConvPlan {
   int C, NC, S, P;

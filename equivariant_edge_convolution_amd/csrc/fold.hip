@@ -544,20 +544,46 @@ constexpr int LDG = HID + 1;                       // row stride of G_l in LDS
 constexpr int GRAM_FLOATS = 4 * HID * LDG;
 
 // G_l[k][k'] for one species pair.  Block (l, four rows k): the degree-l
-// columns of W3 (64 x C) in LDS, one entry per thread, binary64 sums over c.
+// columns of W3 (64 x C) in LDS (16-byte loads where W3 allows, all issued
+// before the first store), one entry per thread, binary64 sums over c.
 constexpr int GRAM_T = 256;
 constexpr int GRAM_BLOCKS = 4 * HID * HID / GRAM_T;
-__global__ void __launch_bounds__(GRAM_T) k_gram(int C, const float* __restrict__ W3, const float* __restrict__ emb,
+template <int C>
+__global__ void __launch_bounds__(GRAM_T) k_gram(const float* __restrict__ W3, const float* __restrict__ emb,
                                                  const float* __restrict__ w_read, float* __restrict__ G) {
-  __shared__ float w3l[HID][128 + 1];  // [k][c], C <= 128
-  __shared__ double d[128];           // 2 w_c h_c^2
-  constexpr int ROWS = GRAM_T / HID;
+  __shared__ float w3l[HID][C + 1];  // [k][c]
+  __shared__ double d[C];            // 2 w_c h_c^2
+  constexpr int ROWS = GRAM_T / HID, Q = C / 4, PER = HID * Q / GRAM_T;
   const int l = blockIdx.x / (HID / ROWS), k0 = ROWS * (blockIdx.x % (HID / ROWS));
-  for (int t = threadIdx.x; t < HID * C; t += GRAM_T) w3l[t / C][t % C] = W3[(size_t)(t / C) * 4 * C + l * C + t % C];
+  float4 v[PER];
+  if ((reinterpret_cast<uintptr_t>(W3) & 15) == 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = threadIdx.x + u * GRAM_T;
+      v[u] = *reinterpret_cast<const float4*>(W3 + (size_t)(t / Q) * 4 * C + l * C + 4 * (t % Q));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = threadIdx.x + u * GRAM_T;
+      const float* q = W3 + (size_t)(t / Q) * 4 * C + l * C + 4 * (t % Q);
+      v[u] = make_float4(q[0], q[1], q[2], q[3]);
+    }
+  }
   for (int c = threadIdx.x; c < C; c += GRAM_T) d[c] = 2.0 * (double)w_read[c] * (double)emb[c] * (double)emb[c];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = threadIdx.x + u * GRAM_T;
+    float* row = &w3l[t / Q][4 * (t % Q)];
+    row[0] = v[u].x;
+    row[1] = v[u].y;
+    row[2] = v[u].z;
+    row[3] = v[u].w;
+  }
   __syncthreads();
   const int k = k0 + threadIdx.x / HID, kk = threadIdx.x % HID;
   double acc = 0.0;
+#pragma unroll 8
   for (int c = 0; c < C; ++c) acc += d[c] * (double)w3l[k][c] * (double)w3l[kk][c];
   G[((size_t)l * HID + k) * HID + kk] = (float)acc;
 }
@@ -922,7 +948,11 @@ void launch_transpose_w3(hipStream_t s, const ConvPlan& p, const eec_model* m, c
 bool fold_fused_supported(const ConvPlan& p) { return p.S == 1; }
 
 void launch_gram(hipStream_t s, const ConvPlan& p, const eec_model* m, char* ws) {
-  k_gram<<<GRAM_BLOCKS, GRAM_T, 0, s>>>(p.C, m->W3, m->emb, m->w_read, (float*)(ws + p.off_w3t));
+  float* G = (float*)(ws + p.off_w3t);
+  if (p.C == 64)
+    k_gram<64><<<GRAM_BLOCKS, GRAM_T, 0, s>>>(m->W3, m->emb, m->w_read, G);
+  else
+    k_gram<128><<<GRAM_BLOCKS, GRAM_T, 0, s>>>(m->W3, m->emb, m->w_read, G);
 }
 
 void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,

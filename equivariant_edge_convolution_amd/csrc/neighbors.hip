@@ -249,6 +249,54 @@ __global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict_
 
 inline int blocks_for(int64_t n, int per) { return (int)std::max<int64_t>(1, (n + per - 1) / per); }
 
+// ---------------------------------------------------------------- skin test
+// Largest squared displacement of any atom from the positions its list was
+// built from, d = x_i - ref_i in binary64 and (dx*dx + dy*dy) + dz*dz with no
+// fused multiply-add, and whether it exceeds half_skin^2.  Non-negative
+// binary64 values order like their bit patterns, so the integer maximum of the
+// per-block results is the same word in whatever order the blocks finish.
+constexpr int SKIN_T = 256;
+constexpr int SKIN_MAX_BLOCKS = 1024;
+
+__global__ void k_skin_clear(unsigned long long* __restrict__ max_r2, int32_t* __restrict__ rebuild) {
+  if (threadIdx.x == 0) {
+    *max_r2 = 0ull;
+    *rebuild = 0;
+  }
+}
+
+__global__ void __launch_bounds__(SKIN_T) k_skin(int32_t n, const double* __restrict__ pos,
+                                                 const double* __restrict__ ref, double hs2,
+                                                 unsigned long long* __restrict__ max_r2,
+                                                 int32_t* __restrict__ rebuild) {
+  __shared__ double part[SKIN_T / 64];
+  double m = 0.0;
+  for (int64_t i = blockIdx.x * (int64_t)SKIN_T + threadIdx.x; i < n; i += (int64_t)gridDim.x * SKIN_T) {
+    double d[3];
+    {
+#pragma clang fp contract(off)
+      d[0] = pos[3 * i + 0] - ref[3 * i + 0];
+      d[1] = pos[3 * i + 1] - ref[3 * i + 1];
+      d[2] = pos[3 * i + 2] - ref[3 * i + 2];
+    }
+    const double r2 = norm2_nofma(d);
+    // a NaN displacement (non-finite input) counts as the largest
+    m = (r2 > m || r2 != r2) ? r2 : m;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double v = __shfl_xor(m, o);
+    m = (v > m || v != v) ? v : m;
+  }
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < SKIN_T / 64; ++w) m = (part[w] > m || part[w] != part[w]) ? part[w] : m;
+    if (m != m) m = __longlong_as_double(0x7ff0000000000000ll);  // NaN -> +inf
+    atomicMax(max_r2, (unsigned long long)__double_as_longlong(m));
+    if (m > hs2) atomicMax(rebuild, 1);
+  }
+}
+
 }  // namespace
 
 NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff) {
@@ -337,6 +385,16 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   }
   if (hipGetLastError() != hipSuccess) { *why = "kernel launch failed"; return EEC_ERR_HIP; }
   return EEC_OK;
+}
+
+void launch_skin_check(hipStream_t s, int32_t n, const double* pos, const double* ref, double half_skin,
+                       double* max_r2, int32_t* rebuild) {
+  auto* m2 = reinterpret_cast<unsigned long long*>(max_r2);
+  k_skin_clear<<<1, 64, 0, s>>>(m2, rebuild);
+  if (n > 0) {
+    const int blocks = (int)std::min<int64_t>(SKIN_MAX_BLOCKS, ((int64_t)n + SKIN_T - 1) / SKIN_T);
+    k_skin<<<blocks, SKIN_T, 0, s>>>(n, pos, ref, half_skin * half_skin, m2, rebuild);
+  }
 }
 
 }  // namespace eec

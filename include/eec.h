@@ -132,9 +132,12 @@ typedef struct {
  *              EEC_ERR_CAPACITY (then it is the capacity required and the CSR
  *              arrays are not written).
  *   workspace  >= eec_neighbors_workspace_bytes(n_atoms, box, cutoff) bytes
- * Synchronises `stream` once (to read E and the validity flags).  The
- * out-of-box, species and coincident-atom checks are made on the device
- * before any CSR array is written. */
+ * Synchronises `stream` once (to read E and the validity flags); the CSR
+ * arrays are written after that, on `stream`, so work on another stream that
+ * reads them must wait for `stream` (an event).  The out-of-box, species and
+ * coincident-atom checks are made on the device before any CSR array is
+ * written.  A list built with a cutoff larger than the model's (a Verlet skin)
+ * serves the compute entry points unchanged: see eec_skin_check. */
 EEC_API eec_status eec_build_neighbors(void *stream, int32_t n_atoms, const double *pos,
                                const double *box, double cutoff,
                                const int32_t *species, int32_t n_species,
@@ -144,6 +147,34 @@ EEC_API eec_status eec_build_neighbors(void *stream, int32_t n_atoms, const doub
 
 EEC_API size_t eec_neighbors_workspace_bytes(int32_t n_atoms, const double *box /*[host][3]*/,
                                      double cutoff);
+
+/* ------------------------------------------------------------------------
+ * eec_skin_check -- the Verlet-skin test of an MD loop that builds its list
+ * with cutoff rc + skin and reuses it while every atom stays within skin / 2
+ * of where it was at the build: then no pair closer than rc can be missing
+ * from the list, and the listed pairs at rc or beyond add exactly zero to
+ * every output of the compute entry points (the envelope and its derivative
+ * vanish there, and the radial network has no bias).  The pages rebuild the
+ * list beside the force call ("FastMACE rewrite screens", OPT2-T04
+ * overlap_rebuild) and try a 0.2 A skin (the research-engine table's skin and
+ * edge-bucket row).
+ *   pos, ref   [n_atoms][3] float64: current positions, and the positions the
+ *              list was built from (the same frame: the list's image shifts
+ *              refer to it, so positions must not be wrapped back into the
+ *              cell between rebuilds; the displacement is taken without the
+ *              minimum image, so an atom wrapped anyway shows a displacement
+ *              of about one box side and is flagged)
+ *   half_skin  >= 0, the largest displacement allowed (skin / 2)
+ *   max_r2     [1] float64 out: max_i (dx*dx + dy*dy) + dz*dz, d = pos_i - ref_i
+ *              in binary64 (no fused multiply-add); +inf if a displacement is
+ *              not a number; 0 when n_atoms == 0
+ *   rebuild    [1] int32 out: 1 if *max_r2 > half_skin * half_skin, else 0
+ * Both outputs are device memory, written on `stream` (two small launches, no
+ * synchronisation); the caller reads them when it needs them (for instance
+ * one step later, so that the loop never waits on the device). */
+EEC_API eec_status eec_skin_check(void *stream, int32_t n_atoms, const double *pos,
+                          const double *ref, double half_skin, double *max_r2,
+                          int32_t *rebuild);
 
 /* ------------------------------------------------------------------------
  * eec_radial_basis -- per-edge geometry, radial basis and harmonics,

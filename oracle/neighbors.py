@@ -26,6 +26,7 @@ printed diamond edge counts (tests/golden/pages_edge_counts.json).
 from __future__ import annotations
 
 import dataclasses
+import math
 import numpy as np
 
 # shift index s = (nx+1)*9 + (ny+1)*3 + (nz+1); ascending s == lexicographic (nx, ny, nz)
@@ -168,3 +169,32 @@ def edge_vectors(pos: np.ndarray, box: np.ndarray, csr: CSR) -> np.ndarray:
     """d_e = (x_j - x_i) + n*L in binary64 (same operation order as the test)."""
     recv = csr.receivers()
     return (pos[csr.col] - pos[recv]) + csr.shift.astype(np.float64) * np.asarray(box)[None, :]
+
+
+def max_displacement2(pos: np.ndarray, ref: np.ndarray) -> float:
+    """Largest squared displacement of any atom since the list was built:
+    max_i (dx*dx + dy*dy) + dz*dz with d = pos_i - ref_i in binary64, no fused
+    multiply-add, no minimum image (the list's image shifts refer to the frame
+    of ``ref``, so an atom wrapped back into the cell must show as moved);
+    +inf if any displacement is not a number; 0.0 for no atoms.
+
+    Verlet skin of an MD loop that reuses its list between rebuilds ("FastMACE
+    rewrite screens", OPT2-T04 overlap_rebuild; the research-engine table's
+    row on a 0.2 A skin)."""
+    pos = np.asarray(pos, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if pos.shape[0] == 0:
+        return 0.0
+    d = pos - ref
+    r2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+    if np.any(np.isnan(r2)):
+        return math.inf
+    return float(r2.max())
+
+
+def needs_rebuild(pos: np.ndarray, ref: np.ndarray, half_skin: float) -> bool:
+    """True iff some atom moved farther than half the skin: a list built with
+    cutoff rc + skin at ``ref`` then may miss a pair closer than rc (two atoms
+    approaching each other head-on close the gap by twice the displacement)."""
+    hs = float(half_skin)
+    return max_displacement2(pos, ref) > hs * hs

@@ -87,3 +87,24 @@ def test_host_side_errors():
                              ctypes.byref(m), ctypes.c_void_p(1 << 25), None, ctypes.c_void_p(1 << 26),
                              None, ctypes.c_void_p((1 << 28) + 64), need)
     assert B.STATUS[st] == "EEC_ERR_WORKSPACE"  # misaligned
+
+
+def test_skin_check_host_side_errors():
+    # every case is rejected before anything is launched
+    L = B.lib()
+    vp = ctypes.c_void_p
+    st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), 0.1, None, vp(1 << 20))
+    assert B.STATUS[st] == "EEC_ERR_NULL"
+    st = L.eec_skin_check(None, 4, None, vp(1 << 17), 0.1, vp(1 << 19), vp(1 << 20))
+    assert B.STATUS[st] == "EEC_ERR_NULL"
+    st = L.eec_skin_check(None, -1, vp(1 << 16), vp(1 << 17), 0.1, vp(1 << 19), vp(1 << 20))
+    assert B.STATUS[st] == "EEC_ERR_SHAPE"
+    for half in (float("nan"), float("inf"), -0.5):
+        st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), half, vp(1 << 19), vp(1 << 20))
+        assert B.STATUS[st] == "EEC_ERR_SHAPE", half
+    st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), 0.1, vp((1 << 19) + 4), vp(1 << 20))
+    assert B.STATUS[st] == "EEC_ERR_SHAPE"  # misaligned max_r2
+    st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), 0.1, vp((1 << 16) + 8), vp(1 << 20))
+    assert B.STATUS[st] == "EEC_ERR_ALIAS"  # max_r2 inside pos
+    st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), 0.1, vp(1 << 19), vp(1 << 19))
+    assert B.STATUS[st] == "EEC_ERR_ALIAS"  # the two outputs overlap

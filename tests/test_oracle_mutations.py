@@ -206,3 +206,30 @@ def test_gram_with_the_wrong_degree_block(monkeypatch):
     monkeypatch.setattr(M, "_gram_orig", M.gram_readout, raising=False)
     monkeypatch.setattr(M, "gram_readout", bad)
     _fails(TM.test_gram_readout, "D64")
+
+
+def test_envelope_not_cut_off_beyond_rc(monkeypatch):
+    # the polynomial continued past x = 1 instead of zero there: skin edges leak
+    import test_oracle_skin as TK
+
+    def bad(x):
+        x = np.asarray(x, np.float64)
+        return 1.0 - 28.0 * x**6 + 48.0 * x**7 - 21.0 * x**8
+
+    monkeypatch.setattr(M, "envelope", bad)
+    _fails(TK.test_skin_edges_add_nothing, "D64")
+
+
+def test_skin_displacement_by_minimum_image(monkeypatch):
+    # minimum image would hide an atom wrapped back into the cell
+    import test_oracle_skin as TK
+    from oracle import neighbors as NB
+
+    def bad(pos, ref):
+        d = np.asarray(pos, np.float64) - np.asarray(ref, np.float64)
+        d -= 10.0 * np.rint(d / 10.0)
+        r2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+        return float(r2.max()) if len(r2) else 0.0
+
+    monkeypatch.setattr(NB, "max_displacement2", bad)
+    _fails(TK.test_wrapped_atom_and_nan_are_flagged)
