@@ -59,9 +59,16 @@ FUSED_FLOP_PER_UNIT = 2 * 16 * 64 * 64 + 2 * 16 * 64
 # Several species (k_fold_multi): per (receiver, sender species) unit the
 # forward's A += h T^T W3 (2 * 16 * 64 * 64) and the backward's M.
 FOLD_FWD_FLOP_PER_UNIT = 2 * 16 * 64 * 64
+# Radial tables (k_fold_table): per edge the Horner evaluation of 64 units and
+# their t-derivatives (degree 10: 2 * 64 * 10 multiply-adds), T = s2^T Y,
+# Ybar = M s2, s2bar = M^T Y and rbar = s2bar . ds2/dr; per receiver as the
+# fused kernel.
+TAB_FLOP_PER_EDGE = 2 * (2 * 64 * 10) + 2048 + 2048 + 2048 + 2 * 64
 
 
 def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int, n_atoms: int = 1 << 30):
+    if variant == "tabulated":
+        return "k_fold_table", "forward", TAB_FLOP_PER_EDGE * n_edges + FUSED_FLOP_PER_UNIT * n_units
     """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
     if variant == "folded" and n_species == 1:
         flop = (FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges + FUSED_FLOP_PER_UNIT * n_units
@@ -321,9 +328,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-variant", action="store_true",
                     help="time only --variant (for profiler runs that should see one kernel family)")
-    ap.add_argument("--variant", default="folded", choices=["direct", "folded"],
+    ap.add_argument("--variant", default="folded", choices=["direct", "folded", "tabulated"],
                     help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
-                         "last radial layer moved past the edge sum (eec_energy_forces_folded)")
+                         "last radial layer moved past the edge sum (eec_energy_forces_folded); "
+                         "tabulated: s2 and ds2/dr from certified radial tables "
+                         "(eec_energy_forces_tabulated, approximate, one species)")
     ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy", "md"],
                     help="energy_forces: the headline call; edge_message: the chunked streaming "
                          "forward (radial rows + message pass), for profiling its kernels; copy: a "
@@ -377,7 +386,8 @@ def main() -> int:
         """Timed region: `steps` calls, with hipEvents around the dominant
         kernel's launch only; then the same number of calls with every phase
         recorded (phases_ms, not part of the timed figure)."""
-        ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=variant)
+        ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=variant,
+                            table=table if variant == "tabulated" else None)
         _, dom_phase, _ = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
         dp = B.PHASES.index(dom_phase)
         ev = B.HipEvents(2 * nph * max(steps, 1))
@@ -402,10 +412,17 @@ def main() -> int:
         ev.close()
         return dt * 1e3 / steps, phase_ms, float(ef.energy.cpu()[0]), dom_ms
 
+    table = None
+    if args.variant == "tabulated" or (cfg.model.n_species == 1 and not args.no_other_variant):
+        table = B.RadialTable(model, 6)
+        cert = [float(x) for x in table.certificate.cpu()]
     ms_per_step, phase_ms, energy, dom_ms = timed(args.variant, args.steps, args.warmup)
-    other = "direct" if args.variant == "folded" else "folded"
+    others = [v for v in ("folded", "direct", "tabulated") if v != args.variant
+              and (v != "tabulated" or table is not None)]
+    other_res = {}
     if not args.no_other_variant:
-        o_ms, o_phase, o_energy, o_dom = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+        for other in others:
+            other_res[other] = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
     def roof(variant, launch_ms):
         kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
@@ -433,10 +450,12 @@ def main() -> int:
                      "traffic": recorded_traffic(kernel, args.config),
                      "flop_per_launch": flop, "launch_ms": launch_ms},
         "variant": args.variant,
-        "variants": {} if args.no_other_variant else {
+        "variants": {
             other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase, "energy": o_energy,
-                    "roofline_kernel": roof(other, o_dom)[0],
-                    "roofline_frac": roof(other, o_dom)[3] / PEAK_FP32_MFMA_TFLOPS}},
+                    "roofline_kernel": roof(other, o_dom)[0], "kernel_ms": o_dom,
+                    "roofline_frac": roof(other, o_dom)[3] / PEAK_FP32_MFMA_TFLOPS,
+                    **({"table_certificate": cert, "approximate": True} if other == "tabulated" else {})}
+            for other, (o_ms, o_phase, o_energy, o_dom) in other_res.items()},
         "phases_ms": phase_ms,
         "neighbors_ms": nb_ms,
         "energy": energy,

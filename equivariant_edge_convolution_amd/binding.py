@@ -33,10 +33,10 @@ SYMBOLS = (
     "eec_build_neighbors", "eec_neighbors_workspace_bytes", "eec_skin_check", "eec_radial_basis",
     "eec_radial_project", "eec_project_workspace_bytes", "eec_edge_message",
     "eec_energy_forces", "eec_energy_forces_folded", "eec_energy_forces_timed", "eec_workspace_bytes",
-    "eec_last_error",
+    "eec_radial_table_floats", "eec_radial_table_levels", "eec_radial_table_build", "eec_energy_forces_tabulated", "eec_last_error",
 )
 PHASES = ("prepare", "forward", "readout", "backward", "scatter")
-VARIANTS = {"direct": 0, "folded": 1}
+VARIANTS = {"direct": 0, "folded": 1, "tabulated": 2}
 
 
 class EECError(RuntimeError):
@@ -60,6 +60,10 @@ class _Graph(ctypes.Structure):
         ("n_atoms", ctypes.c_int32), ("n_edges", ctypes.c_int64), ("row_ptr", ctypes.c_void_p),
         ("col", ctypes.c_void_p), ("shift", ctypes.c_void_p), ("rev", ctypes.c_void_p),
     ]
+
+
+class _Table(ctypes.Structure):
+    _fields_ = [("log2_pieces", ctypes.c_int32), ("coef", ctypes.c_void_p), ("level", ctypes.c_void_p)]
 
 
 _lib = None
@@ -100,7 +104,16 @@ def lib() -> ctypes.CDLL:
     L.eec_energy_forces_folded.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz]
     L.eec_energy_forces_timed.restype = ctypes.c_int
     L.eec_energy_forces_timed.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz,
-                                          i32, P(vp)]
+                                          i32, P(_Table), P(vp)]
+    L.eec_energy_forces_tabulated.restype = ctypes.c_int
+    L.eec_energy_forces_tabulated.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), P(_Table), vp, vp, vp,
+                                              vp, vp, sz]
+    L.eec_radial_table_floats.restype = sz
+    L.eec_radial_table_floats.argtypes = [P(_Model), i32]
+    L.eec_radial_table_build.restype = ctypes.c_int
+    L.eec_radial_table_levels.restype = sz
+    L.eec_radial_table_levels.argtypes = [P(_Model), i32]
+    L.eec_radial_table_build.argtypes = [vp, P(_Model), i32, vp, sz, vp, vp]
     _lib = L
     return L
 
@@ -290,12 +303,39 @@ def edge_message(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, mo
     return A
 
 
+class RadialTable:
+    """eec_radial_table_build: the model's radial tables (device float32) and
+    their certificate (device float64 [2]: value and r-derivative error
+    relative to the local scale)."""
+
+    def __init__(self, model: "Model", log2_pieces: int = 6):
+        m = model.struct()
+        n = int(lib().eec_radial_table_floats(ctypes.byref(m), int(log2_pieces)))
+        nl = int(lib().eec_radial_table_levels(ctypes.byref(m), int(log2_pieces)))
+        if n == 0 or nl == 0:
+            raise EECError(2, "radial_table_build", "log2_pieces out of range")
+        dev = model.W1.device
+        self.log2_pieces = int(log2_pieces)
+        self.coef = torch.empty(n, dtype=torch.float32, device=dev)
+        self.level = torch.empty(nl, dtype=torch.int32, device=dev)
+        self.certificate = torch.empty(2, dtype=torch.float64, device=dev)
+        _check(lib().eec_radial_table_build(_stream(dev), ctypes.byref(m), self.log2_pieces, _ptr(self.coef), n,
+                                            _ptr(self.level), _ptr(self.certificate)), "radial_table_build")
+
+    def struct(self) -> _Table:
+        return _Table(self.log2_pieces, self.coef.data_ptr(), self.level.data_ptr())
+
+
 class EnergyForces:
     """Preallocated outputs + workspace for repeated eec_energy_forces calls."""
 
     def __init__(self, graph: Graph, model: Model, device, atom_energy=True, virial=False,
-                 variant: str = "direct", edge_capacity: int | None = None):
+                 variant: str = "direct", edge_capacity: int | None = None, table: RadialTable | None = None):
         n = graph.n_atoms
+        if (variant == "tabulated") != (table is not None):
+            raise ValueError("the tabulated variant takes a RadialTable, the others none")
+        self.table = table
+        self._t = table.struct() if table is not None else None
         self.variant = VARIANTS[variant]
         self.graph, self.model = graph, model
         self.energy = torch.empty(1, dtype=torch.float32, device=device)
@@ -320,19 +360,24 @@ class EnergyForces:
         args = (s, ctypes.byref(self._g), _ptr(pos), _box(box), _ptr(species), ctypes.byref(self._m),
                 _ptr(self.energy), _ptr(self.atom_energy), _ptr(self.forces), _ptr(self.virial),
                 _ptr(self.workspace), self.workspace.numel())
+        tab = ctypes.byref(self._t) if self._t is not None else None
         if events is None:
-            fn = lib().eec_energy_forces if self.variant == 0 else lib().eec_energy_forces_folded
-            _check(fn(*args), "energy_forces")
+            if self.variant == 2:
+                _check(lib().eec_energy_forces_tabulated(*args[:6], tab, *args[6:]), "energy_forces_tabulated")
+            else:
+                fn = lib().eec_energy_forces if self.variant == 0 else lib().eec_energy_forces_folded
+                _check(fn(*args), "energy_forces")
         else:
             arr = (ctypes.c_void_p * len(events))(*events)
-            _check(lib().eec_energy_forces_timed(*args, self.variant, arr), "energy_forces_timed")
+            _check(lib().eec_energy_forces_timed(*args, self.variant, tab, arr), "energy_forces_timed")
         return self
 
 
 def energy_forces(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, model: Model,
-                  virial: bool = False, variant: str = "direct"):
-    """eec_energy_forces (variant "direct") or eec_energy_forces_folded ("folded")."""
-    ef = EnergyForces(graph, model, pos.device, atom_energy=True, virial=virial, variant=variant)
+                  virial: bool = False, variant: str = "direct", table: RadialTable | None = None):
+    """eec_energy_forces (variant "direct"), eec_energy_forces_folded ("folded")
+    or eec_energy_forces_tabulated ("tabulated", with ``table``)."""
+    ef = EnergyForces(graph, model, pos.device, atom_energy=True, virial=virial, variant=variant, table=table)
     ef(pos, box, species)
     out = dict(energy=ef.energy, atom_energy=ef.atom_energy, forces=ef.forces)
     if virial:

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libeec.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["neighbors.hip", "radial.hip", "fold.hip", "conv.hip", "api.hip"]
+SOURCES = ["neighbors.hip", "radial.hip", "fold.hip", "table.hip", "conv.hip", "api.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
     "--offload-arch=gfx950",

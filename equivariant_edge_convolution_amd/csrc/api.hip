@@ -250,24 +250,37 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
                                      const double* box, const int32_t* species, const eec_model* m,
                                      float* energy, float* atom_energy, float* forces, float* virial,
                                      void* workspace, size_t workspace_bytes, int32_t variant,
-                                     void* const* events) {
-  if (variant != EEC_VARIANT_DIRECT && variant != EEC_VARIANT_FOLDED)
+                                     const eec_radial_table* tab, void* const* events) {
+  if (variant != EEC_VARIANT_DIRECT && variant != EEC_VARIANT_FOLDED && variant != EEC_VARIANT_TABULATED)
     return fail(EEC_ERR_SHAPE, "unknown variant");
   TRY(check_graph(g));
   TRY(check_model(m));
   TRY(check_box(box, m->cutoff));
   if (energy == nullptr) return fail(EEC_ERR_NULL, "energy is NULL");
   if (g->n_atoms > 0 && (!pos || !species || !forces)) return fail(EEC_ERR_NULL, "pos, species or forces is NULL");
+  const bool tabulated = variant == EEC_VARIANT_TABULATED;
+  if (tabulated) {
+    if (tab == nullptr || tab->coef == nullptr || tab->level == nullptr)
+      return fail(EEC_ERR_NULL, "radial table is NULL");
+    if (tab->log2_pieces < TAB_MIN_LOG2 || tab->log2_pieces > TAB_MAX_LOG2)
+      return fail(EEC_ERR_SHAPE, "radial table log2_pieces out of range");
+    if (m->n_species != 1) return fail(EEC_ERR_SHAPE, "the tabulated variant takes one species");
+    if (((uintptr_t)tab->coef & 7) != 0) return fail(EEC_ERR_SHAPE, "radial table must be 8-byte aligned");
+  }
   const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
   TRY(check_ws(workspace, workspace_bytes, p.bytes));
   const size_t N = (size_t)g->n_atoms;
+  const Span tspan = tabulated ? span(tab->coef, 4 * table_floats(m->n_species, tab->log2_pieces), "radial table")
+                               : span(nullptr, 0, "radial table");
+  const Span lspan = tabulated ? span(tab->level, 4 * table_levels(m->n_species, tab->log2_pieces), "table levels")
+                               : span(nullptr, 0, "table levels");
   TRY(check_alias({span(energy, 4, "energy"), span(atom_energy, 4 * N, "atom_energy"),
                    span(forces, 12 * N, "forces"), span(virial, 36, "virial"),
                    span(workspace, workspace_bytes, "workspace")},
                   {span(pos, 24 * N, "pos"), span(species, 4 * N, "species"), graph_span_rp(g),
                    graph_span_col(g), graph_span_shift(g), graph_span_rev(g), model_span(m->W1, m, 1),
                    model_span(m->W2, m, 2), model_span(m->W3, m, 3), model_span(m->emb, m, 4),
-                   model_span(m->w_read, m, 5)}));
+                   model_span(m->w_read, m, 5), tspan, lspan}));
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int k) {
     if (events != nullptr && events[k] != nullptr) hipEventRecord((hipEvent_t)events[k], s);
@@ -280,6 +293,23 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   float* Yc = (float*)(ws + p.off_Y);
   float* gbuf = (float*)(ws + p.off_g);
   const bool folded = variant == EEC_VARIANT_FOLDED;
+  if (tabulated) {
+    // one kernel per receiver, s2 and ds2/dr from the radial table
+    mark(2 * EEC_PHASE_PREPARE);
+    launch_gram(s, p, m, ws);
+    mark(2 * EEC_PHASE_PREPARE + 1);
+    mark(2 * EEC_PHASE_FORWARD);
+    launch_fold_table(s, p, g, pos, b, m->cutoff, m, tab->log2_pieces, tab->coef, tab->level, ei, gbuf, ws);
+    mark(2 * EEC_PHASE_FORWARD + 1);
+    for (int k : {EEC_PHASE_READOUT, EEC_PHASE_BACKWARD}) {
+      mark(2 * k);
+      mark(2 * k + 1);
+    }
+    mark(2 * EEC_PHASE_SCATTER);
+    launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
+    mark(2 * EEC_PHASE_SCATTER + 1);
+    return launched("energy_forces_tabulated");
+  }
   if (folded && fold_fused_supported(p)) {
     // one kernel per receiver from geometry to dE/dd; no preparation, no A
     mark(2 * EEC_PHASE_PREPARE);
@@ -354,7 +384,7 @@ eec_status eec_energy_forces(void* stream, const eec_graph* g, const double* pos
                              const int32_t* species, const eec_model* m, float* energy, float* atom_energy,
                              float* forces, float* virial, void* workspace, size_t workspace_bytes) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
-                            workspace_bytes, EEC_VARIANT_DIRECT, nullptr);
+                            workspace_bytes, EEC_VARIANT_DIRECT, nullptr, nullptr);
 }
 
 eec_status eec_energy_forces_folded(void* stream, const eec_graph* g, const double* pos, const double* box,
@@ -362,15 +392,56 @@ eec_status eec_energy_forces_folded(void* stream, const eec_graph* g, const doub
                                     float* atom_energy, float* forces, float* virial, void* workspace,
                                     size_t workspace_bytes) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
-                            workspace_bytes, EEC_VARIANT_FOLDED, nullptr);
+                            workspace_bytes, EEC_VARIANT_FOLDED, nullptr, nullptr);
 }
 
 eec_status eec_energy_forces_timed(void* stream, const eec_graph* g, const double* pos, const double* box,
                                    const int32_t* species, const eec_model* m, float* energy,
                                    float* atom_energy, float* forces, float* virial, void* workspace,
-                                   size_t workspace_bytes, int32_t variant, void* const* events) {
+                                   size_t workspace_bytes, int32_t variant, const eec_radial_table* tab,
+                                   void* const* events) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
-                            workspace_bytes, variant, events);
+                            workspace_bytes, variant, tab, events);
+}
+
+eec_status eec_energy_forces_tabulated(void* stream, const eec_graph* g, const double* pos, const double* box,
+                                       const int32_t* species, const eec_model* m, const eec_radial_table* tab,
+                                       float* energy, float* atom_energy, float* forces, float* virial,
+                                       void* workspace, size_t workspace_bytes) {
+  return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
+                            workspace_bytes, EEC_VARIANT_TABULATED, tab, nullptr);
+}
+
+size_t eec_radial_table_floats(const eec_model* m, int32_t log2_pieces) {
+  if (m == nullptr || m->n_species < 1 || m->n_species > 4 || log2_pieces < TAB_MIN_LOG2 ||
+      log2_pieces > TAB_MAX_LOG2)
+    return 0;
+  return table_floats(m->n_species, log2_pieces);
+}
+
+size_t eec_radial_table_levels(const eec_model* m, int32_t log2_pieces) {
+  if (m == nullptr || m->n_species < 1 || m->n_species > 4 || log2_pieces < TAB_MIN_LOG2 ||
+      log2_pieces > TAB_MAX_LOG2)
+    return 0;
+  return table_levels(m->n_species, log2_pieces);
+}
+
+eec_status eec_radial_table_build(void* stream, const eec_model* m, int32_t log2_pieces, float* coef,
+                                  size_t coef_floats, int32_t* level, double* certificate) {
+  TRY(check_model(m));
+  if (log2_pieces < TAB_MIN_LOG2 || log2_pieces > TAB_MAX_LOG2)
+    return fail(EEC_ERR_SHAPE, "log2_pieces out of range");
+  if (coef == nullptr || level == nullptr) return fail(EEC_ERR_NULL, "coef or level is NULL");
+  const size_t need = table_floats(m->n_species, log2_pieces);
+  if (coef_floats < need) return fail(EEC_ERR_SHAPE, "coef is smaller than eec_radial_table_floats");
+  if (((uintptr_t)coef & 7) != 0 || ((uintptr_t)certificate & 7) != 0)
+    return fail(EEC_ERR_SHAPE, "coef and certificate must be 8-byte aligned");
+  if (((uintptr_t)level & 3) != 0) return fail(EEC_ERR_SHAPE, "level must be 4-byte aligned");
+  TRY(check_alias({span(coef, 4 * need, "coef"), span(level, 4 * table_levels(m->n_species, log2_pieces), "level"),
+                   span(certificate, 16, "certificate")},
+                  {model_span(m->W1, m, 1), model_span(m->W2, m, 2)}));
+  launch_table_build((hipStream_t)stream, m, log2_pieces, coef, level, certificate);
+  return launched("radial_table_build");
 }
 
 }  // extern "C"

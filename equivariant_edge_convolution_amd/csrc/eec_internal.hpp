@@ -137,6 +137,28 @@ void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
                        char* ws);
 
+// Radial tables (one species pair after another): polynomials of degree
+// TAB_DEG on the 2^d(c) sub-pieces of each of 2^log2_pieces coarse pieces of
+// [0, rc]; coefficients [pair][c][f < TAB_SUB][m = 0..TAB_DEG][unit j % 32][j / 32]
+// float32 (slots f >= 2^d(c) unused), levels d [pair][c] int32.
+constexpr int TAB_DEG = 10;
+constexpr int TAB_NC = TAB_DEG + 1;
+constexpr int TAB_DMAX = 4, TAB_SUB = 1 << TAB_DMAX;
+constexpr double TAB_TOL = 1e-8;  // binary64 interpolation error that fixes a piece's level
+constexpr int TAB_MIN_LOG2 = 2, TAB_MAX_LOG2 = 10;
+size_t table_floats(int n_species, int log2_pieces);
+size_t table_levels(int n_species, int log2_pieces);
+// Builds every pair's table; cert (device, 2 doubles, or NULL) receives the
+// largest value and r-derivative errors of the float32 table against binary64,
+// relative to the local scale.
+void launch_table_build(hipStream_t s, const eec_model* m, int log2_pieces, float* tab, int32_t* level,
+                        double* cert);
+// One species: the folded call per receiver in one kernel with s2 and ds2/dr
+// from the table (needs launch_gram first on the stream, as launch_fold_fused).
+void launch_fold_table(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const eec_model* m, int log2_pieces, const float* tab,
+                       const int32_t* level, float* ei, float* gout, char* ws);
+
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace eec

@@ -707,6 +707,299 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   }
 }
 
+// ------------------------------------------------------------------ radial tables
+// The one-species fused call with s2 and ds2/dr read from the radial tables
+// (piecewise polynomials of the chain r -> s2, degree TAB_DEG in the piece
+// variable t) in place of the basis, the first two layers and their SiLUs:
+// the forward tile evaluates s2 and ds2/dr by Horner's rule (lane s: hidden
+// units s and s + 32 of 16 edges, the layout the second layer leaves), keeps
+// both in the stash rows, and accumulates T as the network kernel does; the
+// backward tile takes rbar = sum_k s2bar_k ds2_k/dr directly.  An edge at or
+// beyond the table's end (r >= rc) contributes exactly zero.
+struct TabArgs {
+  const float2* tab;     // [coarse c][sub-piece f < TAB_SUB][m][32] pairs (hidden j, j + 32)
+  const int32_t* level;  // [coarse c] sub-pieces 2^level
+  double inv_h0;         // 2^K / rc: r -> r / h0
+  int n_coarse;
+};
+
+// Sub-piece and local variable of an edge at distance r (binary64, then
+// float32): u = r / h0, coarse c = floor(u), w = (u - c) 2^d(c), f = floor(w),
+// t = 2 (w - f) - 1 in [-1, 1), dt/dr = 2^(d+1) / h0.  Returned as (t, slot
+// c TAB_SUB + f or -1 for "no value", dt/dr, 0).
+__device__ __forceinline__ float4 tab_locate(const TabArgs& ta, double r, bool valid) {
+  const double u = r * ta.inv_h0;
+  const double cf = floor(u);
+  const bool in_range = valid && cf >= 0.0 && cf < (double)ta.n_coarse;
+  const int c = in_range ? (int)cf : 0;
+  const int d = min(max(ta.level[c], 0), TAB_DMAX);
+  const double w = ldexp(u - cf, d);
+  const double ff = fmin(floor(w), (double)((1 << d) - 1));
+  const float t = in_range ? (float)(2.0 * (w - ff) - 1.0) : 0.f;
+  const int slot = in_range ? c * TAB_SUB + (int)ff : -1;
+  return make_float4(t, __int_as_float(slot), (float)ldexp(2.0 * ta.inv_h0, d), 0.f);
+}
+
+// Value and t-derivative of the pair of units at `c` (TAB_NC coefficients, 32 float2 apart).
+__device__ __forceinline__ void tab_horner(const float2* __restrict__ c, float t, float2& v, float2& d) {
+  float2 cc[TAB_NC];
+#pragma unroll
+  for (int m = 0; m < TAB_NC; ++m) cc[m] = c[32 * m];
+  v = cc[TAB_DEG];
+  d = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int m = TAB_DEG - 1; m >= 0; --m) {
+    d.x = d.x * t + v.x;
+    d.y = d.y * t + v.y;
+    v.x = v.x * t + cc[m].x;
+    v.y = v.y * t + cc[m].y;
+  }
+}
+
+__device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const Recv& xi, const TabArgs& ta, float4* tp,
+                                             float (*ysm)[NLM + 1], int q0, int qa, int qb, int s, int h,
+                                             f32x4 T[4], float* zs) {
+  const bool valid = q0 + s < qb;
+  const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(nullptr, q0, qa, qb, s)), xi.x);
+  if (zs != nullptr && valid && h == 0) {
+    float* row = zs + s * ZROW + 2 * HID;
+    float rw[2];
+    __builtin_memcpy(rw, &g.r, sizeof(double));
+    *reinterpret_cast<float4*>(row) = make_float4(g.ux, g.uy, g.uz, g.inv_r);
+    *reinterpret_cast<float2*>(row + 4) = make_float2(rw[0], rw[1]);
+  }
+  if (h == 0) tp[s] = tab_locate(ta, g.r, valid);
+  {
+    float Y[16];
+    sph16(g.ux, g.uy, g.uz, Y);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ysm[s][8 * h + k] = valid ? (h ? Y[8 + k] : Y[k]) : 0.f;  // static indices
+  }
+  wave_sync_lds();
+  // s2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s.
+  // Edges in pairs, the coefficients of the next pair loading while this
+  // pair's Horner steps run (a scheduling fence after each pair keeps the
+  // look-ahead at one pair, within the registers).  The stash rows are
+  // written as they come, padding rows too (a tile's 32 rows exist; rows past
+  // the unit's end are never read), so no lane-dependent branch splits the
+  // sequence.
+  f32x16 a[2];
+  float2 cc[2][2][TAB_NC];
+  float4 loc[2][2];
+  auto fetch = [&](int g, float2 (&dst)[2][TAB_NC], float4 (&lc)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      lc[q] = tp[fperm(2 * g + q) + 4 * h];
+      const float2* c = ta.tab + (size_t)max(__float_as_int(lc[q].y), 0) * TAB_NC * 32 + s;
+#pragma unroll
+      for (int m = 0; m < TAB_NC; ++m) dst[q][m] = c[32 * m];
+    }
+  };
+  fetch(0, cc[0], loc[0]);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g + 1 < 8) fetch(g + 1, cc[(g + 1) & 1], loc[(g + 1) & 1]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 2 * g + q;
+      const float4 e = loc[g & 1][q];
+      const float on = __float_as_int(e.y) >= 0 ? 1.f : 0.f;
+      const float2* c = cc[g & 1][q];
+      float2 v = c[TAB_DEG], d = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int m = TAB_DEG - 1; m >= 0; --m) {
+        d.x = d.x * e.x + v.x;
+        d.y = d.y * e.x + v.y;
+        v.x = v.x * e.x + c[m].x;
+        v.y = v.y * e.x + c[m].y;
+      }
+      a[0][r] = v.x * on;
+      a[1][r] = v.y * on;
+      if (zs != nullptr) {
+        float* row = zs + (fperm(r) + 4 * h) * ZROW + s;
+        row[0] = d.x * e.z * on;
+        row[32] = d.y * e.z * on;
+        row[HID] = a[0][r];
+        row[HID + 32] = a[1][r];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // T[hidden][lm] += s2^T Y over the tile on 16x16x4 tiles (as fwd_tile)
+  {
+    const int j = s & 15, qk = (s >> 4) + 2 * h;
+    const float* yrow = &ysm[8 * (qk & 1) + 4 * (qk >> 1)][j];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int rr = 0; rr < 12; rr = (rr == 3 ? 8 : rr + 1)) {
+        float lo = a[m][rr], hi = a[m][rr + 4];
+        swap_rows16(lo, hi);
+        const float yv = yrow[fperm(rr) * (NLM + 1)];
+        T[2 * m] = mfma16(lo, yv, T[2 * m]);
+        T[2 * m + 1] = mfma16(hi, yv, T[2 * m + 1]);
+      }
+    pipeline_lds_mfma<32, 2, 6>();
+  }
+  wave_sync_lds();
+}
+
+__device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, const TabArgs& ta,
+                                             float (*msm)[HID + 1], float (*ybsm)[NLM + 1], int q0, int qa,
+                                             int qb, int s, int h, float* __restrict__ gout, const float* zs) {
+  const bool valid = q0 + s < qb;
+  const int64_t e = tile_edge(nullptr, q0, qa, qb, s);
+  Geo g;
+  f32x16 ds[2], s2[2];  // ds2/dr and s2, edges on N: register 4j + i of tile m = hidden 4h + 32m + 8j + i
+  if (zs != nullptr) {
+    const float* row = zs + (valid ? s : 0) * ZROW;
+    const float4 u = *reinterpret_cast<const float4*>(row + 2 * HID);
+    const float2 rw = *reinterpret_cast<const float2*>(row + 2 * HID + 4);
+    g.ux = u.x;
+    g.uy = u.y;
+    g.uz = u.z;
+    g.inv_r = u.w;
+    __builtin_memcpy(&g.r, &rw, sizeof(double));
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v1 = *reinterpret_cast<const float4*>(row + 4 * h + 32 * m + 8 * j);
+        const float4 v2 = *reinterpret_cast<const float4*>(row + HID + 4 * h + 32 * m + 8 * j);
+        ds[m][4 * j] = v1.x; ds[m][4 * j + 1] = v1.y; ds[m][4 * j + 2] = v1.z; ds[m][4 * j + 3] = v1.w;
+        s2[m][4 * j] = v2.x; s2[m][4 * j + 1] = v2.y; s2[m][4 * j + 2] = v2.z; s2[m][4 * j + 3] = v2.w;
+      }
+  } else {
+    g = geo_from_raw(in, edge_raw(in, e), xi.x);
+    const float4 loc = tab_locate(ta, g.r, valid);
+    const int piece = __float_as_int(loc.y);
+    const float on = piece >= 0 ? 1.f : 0.f;
+    const float2* c = ta.tab + (size_t)max(piece, 0) * TAB_NC * 32 + 4 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float2 v, d;
+        tab_horner(c + 8 * j + i, loc.x, v, d);  // units 4h + 8j + i and + 32
+        s2[0][4 * j + i] = v.x * on;
+        s2[1][4 * j + i] = v.y * on;
+        ds[0][4 * j + i] = d.x * loc.z * on;
+        ds[1][4 * j + i] = d.y * loc.z * on;
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k] on 16x16x4 tiles (as bwd_tile)
+  f32x4 yb[2];
+  yb[0] = zero4();
+  yb[1] = zero4();
+  {
+    const int j = s & 15, qk = (s >> 4) + 2 * h;
+    const float* mrow = &msm[j][8 * (qk & 1) + 4 * (qk >> 1)];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int rr = 0; rr < 12; rr = (rr == 3 ? 8 : rr + 1)) {
+        float lo = s2[mm][rr], hi = s2[mm][rr + 4];
+        swap_rows16(lo, hi);
+        const float bv = mrow[32 * mm + fperm(rr)];
+        yb[0] = mfma16(lo, bv, yb[0]);
+        yb[1] = mfma16(hi, bv, yb[1]);
+      }
+    pipeline_lds_mfma<32, 2, 6>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // s2bar[k][edge] = sum_lm M[lm][k] Y[edge][lm]  (edges on N)
+  f32x16 sb[2];
+  sb[0] = zero16();
+  sb[1] = zero16();
+  {
+    float Y[16];
+    sph16(g.ux, g.uy, g.uz, Y);
+    const float* mc = &msm[h][s];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float bv = h ? Y[2 * ks + 1] : Y[2 * ks];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) sb[m] = mfma32(mc[2 * ks * (HID + 1) + 32 * m], bv, sb[m]);
+    }
+    pipeline_lds_mfma<16, 2, 6>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int l = s + 32 * h;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ybsm[16 * b + 4 * (l >> 4) + i][l & 15] = yb[b][i];
+  }
+  wave_sync_lds();
+  float G[3];
+  {
+    float ybe[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ybe[k] = ybsm[s][k];
+    sph16_grad_dot(g.ux, g.uy, g.uz, ybe, G);
+  }
+  float rbar = 0.f;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rbar += sb[m][r] * ds[m][r];
+  rbar += __shfl_xor(rbar, 32);
+  const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
+  if (valid && h == 0) {
+    gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
+    gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
+    gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+  }
+  wave_sync_lds();
+}
+
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float* __restrict__ ei,
+             float* __restrict__ gout, float* __restrict__ stash) {
+  __shared__ float gs[GRAM_FLOATS];
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
+  __shared__ float4 tpb[W][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const WaveLds<C> L(wbuf[wave]);
+  const int N = un.n_atoms;
+  const int nbp = (N + W - 1) / W;
+  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) gs[(t >> 6) * LDG + (t & 63)] = G[t];
+  __syncthreads();
+  for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
+    const int i = b * W + wave;
+    if (i >= N) continue;
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
+    const Recv xi = recv_pos(in, i);
+    float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      fwd_tile_tab(in, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
+    wave_sync_lds();
+    float macc[NLM];
+    const float* g = gs + lane * LDG;
+    const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return g[l * HID * LDG + kk]; }, macc);
+    if (lane == 0) ei[i] = e2;
+    if (qb <= qa) continue;
+    wave_sync_lds();  // msm overlays tsm
+#pragma unroll
+    for (int lm = 0; lm < NLM; ++lm) L.msm[lm][lane] = macc[lm];
+    wave_sync_lds();
+    for (int q0 = qa; q0 < qb; q0 += 32)
+      bwd_tile_tab(in, xi, ta, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
+  }
+}
+
 // ------------------------------------------------------------------ fused (several species)
 // Two or three species: one wave per receiver, workgroups taking batches of
 // receivers of one species (atoms in species order).  For each sender species
@@ -901,6 +1194,25 @@ int multi_grid(const ConvPlan& p) {
 }  // namespace
 
 bool fold_multi_supported(const ConvPlan& p) { return p.S >= 2 && p.S <= MULTI_MAX_S; }
+
+void launch_fold_table(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
+                       double cutoff, const eec_model* m, int log2_pieces, const float* tab,
+                       const int32_t* level, float* ei, float* gout, char* ws) {
+  if (p.N == 0) return;
+  const float* G = (const float*)(ws + p.off_w3t);
+  float* stash = (float*)(ws + p.off_stash);
+  const EdgeIn in = make_in_f(p, g, pos, box, cutoff, nullptr);
+  const Units un = make_units(p, g, nullptr, ws);
+  TabArgs ta;
+  ta.tab = reinterpret_cast<const float2*>(tab);
+  ta.level = level;
+  ta.n_coarse = 1 << log2_pieces;
+  ta.inv_h0 = (double)ta.n_coarse / m->cutoff;
+  if (p.C == 64)
+    k_fold_table<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
+  else
+    k_fold_table<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
+}
 
 size_t fold_stash_bytes(const ConvPlan& p) {
   int waves = 0;

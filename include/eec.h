@@ -257,8 +257,68 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
                                     size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
- * eec_energy_forces_timed -- eec_energy_forces (variant EEC_VARIANT_DIRECT) or
- * eec_energy_forces_folded (EEC_VARIANT_FOLDED), with hipEvent_t handles
+ * Radial tables -- the radial chain up to the folded last layer,
+ * r -> s2(r) = silu(silu(b(r) W1) W2) (hidden width 64, per ordered species
+ * pair), as piecewise polynomials of degree 10 on dyadic pieces of
+ * [0, cutoff] ("FastMACE rewrite screens", OPT6-T05 radial_tables:
+ * per-species-pair degree-10 Chebyshev tables on dyadic pieces, values and
+ * r-derivatives certified against binary64, opt-in and float32 only;
+ * OPT6-T04: their accuracy premise).  Approximate: results differ from
+ * eec_energy_forces_folded by the table error, which the certificate bounds.
+ *
+ * Pieces: 2^log2_pieces coarse pieces of width h0 = cutoff / 2^log2_pieces;
+ * coarse piece c is split into 2^d(c) equal sub-pieces, d(c) in [0, 4] the
+ * smallest level at which the binary64 interpolants are within 1e-8 of the
+ * network (values and r-derivatives, relative to the local scale) at 16
+ * points per sub-piece; the short-range pieces, where the chain is largest
+ * and steepest, take the finer levels.
+ *
+ * eec_radial_table_build -- builds every pair's table in binary64 on the
+ * device: each sub-piece interpolated at the 11 Chebyshev points of the
+ * first kind, the interpolant stored in float32 in power form in the
+ * sub-piece variable t in [-1, 1], r = c h0 + (f + (t + 1) / 2) h0 / 2^d(c):
+ *   coef[p][c][f][m][j % 32][j / 32] = a_m of unit j,  s2_j(r) ~ sum_m a_m t^m
+ *   (16 sub-piece slots per coarse piece, f < 2^d(c) used), level[p][c] = d(c).
+ *   m            the model (W1, W2 and the cutoff are read)
+ *   log2_pieces  in [2, 10]; 6 is the default of the binding
+ *   coef         device float32, coef_floats >= eec_radial_table_floats(m, log2_pieces)
+ *   level        device int32 [eec_radial_table_levels(m, log2_pieces)]
+ *   certificate  device double[2] or NULL: the largest error of the stored
+ *                table against the binary64 network over 16 points per
+ *                sub-piece, [0] for values and [1] for r-derivatives, each
+ *                relative to the largest magnitude of that unit's value
+ *                (derivative) over the sub-piece; written on the stream.
+ * No synchronisation. */
+typedef struct {
+  int32_t log2_pieces;
+  const float *coef;    /* as written by eec_radial_table_build for the same model */
+  const int32_t *level;
+} eec_radial_table;
+
+EEC_API size_t eec_radial_table_floats(const eec_model *m, int32_t log2_pieces);
+EEC_API size_t eec_radial_table_levels(const eec_model *m, int32_t log2_pieces);
+
+EEC_API eec_status eec_radial_table_build(void *stream, const eec_model *m, int32_t log2_pieces,
+                                  float *coef, size_t coef_floats, int32_t *level,
+                                  double *certificate);
+
+/* eec_energy_forces_tabulated -- the outputs of eec_energy_forces_folded, one
+ * species, with s2 and ds2/dr of every edge read from `tab` (built for this
+ * model) instead of the basis and the first two layers: per edge a Horner
+ * evaluation of 64 units and their derivatives replaces two dense layers and
+ * their SiLUs in both passes.  Edges at or beyond the cutoff add exactly zero.
+ * Arguments as eec_energy_forces; same workspace size.  EEC_ERR_SHAPE for
+ * more than one species. */
+EEC_API eec_status eec_energy_forces_tabulated(void *stream, const eec_graph *g, const double *pos,
+                                       const double *box /*[host][3]*/, const int32_t *species,
+                                       const eec_model *m, const eec_radial_table *tab,
+                                       float *energy, float *atom_energy, float *forces,
+                                       float *virial, void *workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
+ * eec_energy_forces_timed -- eec_energy_forces (variant EEC_VARIANT_DIRECT),
+ * eec_energy_forces_folded (EEC_VARIANT_FOLDED) or eec_energy_forces_tabulated
+ * (EEC_VARIANT_TABULATED, with `tab`; NULL otherwise), with hipEvent_t handles
  * (created by the caller, e.g. with hipEventCreate) recorded on `stream` around
  * each phase: events[2k] before and events[2k+1] after phase k, for
  *   k = EEC_PHASE_PREPARE   receiver index and pair grouping, and for the
@@ -268,8 +328,9 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  *                           species and the atoms in species order),
  *       EEC_PHASE_FORWARD   radial network + message (one kernel, or the
  *                           radial-row chunks and message passes; folded,
- *                           one to three species: the single fused kernel
- *                           launch, forward, readout and backward),
+ *                           one to three species, and tabulated: the single
+ *                           fused kernel launch, forward, readout and
+ *                           backward),
  *       EEC_PHASE_READOUT   per-atom energies and dE/dA (folded, one to
  *                           three species: empty),
  *       EEC_PHASE_BACKWARD  the streaming backward (one kernel launch;
@@ -280,14 +341,14 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * NULL records nothing.  Results are bit for bit those of the untimed call. */
 enum { EEC_PHASE_PREPARE = 0, EEC_PHASE_FORWARD = 1, EEC_PHASE_READOUT = 2,
        EEC_PHASE_BACKWARD = 3, EEC_PHASE_SCATTER = 4, EEC_N_PHASES = 5 };
-enum { EEC_VARIANT_DIRECT = 0, EEC_VARIANT_FOLDED = 1 };
+enum { EEC_VARIANT_DIRECT = 0, EEC_VARIANT_FOLDED = 1, EEC_VARIANT_TABULATED = 2 };
 
 EEC_API eec_status eec_energy_forces_timed(void *stream, const eec_graph *g, const double *pos,
                                    const double *box /*[host][3]*/, const int32_t *species,
                                    const eec_model *m, float *energy, float *atom_energy,
                                    float *forces, float *virial, void *workspace,
                                    size_t workspace_bytes, int32_t variant,
-                                   void *const *events);
+                                   const eec_radial_table *tab, void *const *events);
 
 EEC_API size_t eec_workspace_bytes(int32_t n_atoms, int64_t n_edges, const eec_model *m);
 

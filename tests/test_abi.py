@@ -108,3 +108,31 @@ def test_skin_check_host_side_errors():
     assert B.STATUS[st] == "EEC_ERR_ALIAS"  # max_r2 inside pos
     st = L.eec_skin_check(None, 4, vp(1 << 16), vp(1 << 17), 0.1, vp(1 << 19), vp(1 << 19))
     assert B.STATUS[st] == "EEC_ERR_ALIAS"  # the two outputs overlap
+
+
+def test_radial_table_host_side_errors():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    m = _model_struct(fake_ptr=1 << 20)
+    assert L.eec_radial_table_floats(ctypes.byref(m), 1) == 0  # log2_pieces out of range
+    assert L.eec_radial_table_levels(ctypes.byref(m), 11) == 0
+    n = L.eec_radial_table_floats(ctypes.byref(m), 6)
+    assert n == 64 * 16 * 11 * 64 and L.eec_radial_table_levels(ctypes.byref(m), 6) == 64
+    st = L.eec_radial_table_build(None, ctypes.byref(m), 1, vp(1 << 24), n, vp(1 << 26), None)
+    assert B.STATUS[st] == "EEC_ERR_SHAPE"
+    st = L.eec_radial_table_build(None, ctypes.byref(m), 6, None, n, vp(1 << 26), None)
+    assert B.STATUS[st] == "EEC_ERR_NULL"
+    st = L.eec_radial_table_build(None, ctypes.byref(m), 6, vp(1 << 24), n - 1, vp(1 << 26), None)
+    assert B.STATUS[st] == "EEC_ERR_SHAPE"  # too small
+    st = L.eec_radial_table_build(None, ctypes.byref(m), 6, vp(1 << 20), n, vp(1 << 26), None)
+    assert B.STATUS[st] == "EEC_ERR_ALIAS"  # coef over the weights
+    # the tabulated call: a NULL table, and several species
+    g = B._Graph(4, 0, 4096, None, None, None)
+    box = (ctypes.c_double * 3)(7.2, 7.2, 7.2)
+    args = (None, ctypes.byref(g), vp(1 << 16), box, vp(1 << 17), ctypes.byref(m))
+    outs = (vp(1 << 25), None, vp(1 << 26), None, vp(1 << 28), 1 << 24)
+    assert B.STATUS[L.eec_energy_forces_tabulated(*args, None, *outs)] == "EEC_ERR_NULL"
+    m3 = _model_struct(n_species=3, fake_ptr=1 << 20)
+    t = B._Table(6, 1 << 29, 1 << 30)
+    args3 = (None, ctypes.byref(g), vp(1 << 16), box, vp(1 << 17), ctypes.byref(m3))
+    assert B.STATUS[L.eec_energy_forces_tabulated(*args3, ctypes.byref(t), *outs)] == "EEC_ERR_SHAPE"

@@ -1,0 +1,156 @@
+"""Radial tables on the GPU ("FastMACE rewrite screens", OPT6-T05 and OPT6-T04).
+
+The device-built tables against the oracle's: every coarse piece's level
+equal (or, where the two binary64 error estimates straddle the tolerance,
+both within 2 % of it), every kept coefficient within 3e-7 of its piece's
+largest coefficient (float32 storage), and the certificate equal to the one
+the oracle computes from the same stored coefficients.  The float32 table is
+more accurate than the float32 network (the pages' certificate ratio < 1).
+The tabulated energy/force call against the float64 oracle of the exact
+network at the same bars as the other variants (energy 1e-5 relative, forces
+max|dF| <= 1e-4 RMS(F)), on a skin list too, and bit for bit repeatable."""
+import numpy as np
+import pytest
+import torch
+
+import eec_inputs as I
+from equivariant_edge_convolution_amd import binding as B
+from oracle import model as M
+from oracle import neighbors as NB
+from oracle import tables as TB
+
+from gpu_util import DEV, device_inputs, graph_for, np_, rms, say
+
+pytestmark = pytest.mark.gpu
+
+_REF = {}
+
+
+def _oracle_table(name, K):
+    key = (name, K)
+    if key not in _REF:
+        m = I.make_config(name).model
+        _REF[key] = [TB.build_pair(TB.pair_chain(m, p), m.cutoff, K) for p in range(m.n_species ** 2)]
+    return _REF[key]
+
+
+def _gpu_table(model, n_pairs, K):
+    t = B.RadialTable(model, K)
+    nc = 1 << K
+    coef = np_(t.coef).reshape(n_pairs, nc, 1 << TB.DMAX, TB.DEG + 1, 32, 2)
+    coef = np.concatenate([coef[..., 0], coef[..., 1]], axis=-1)  # [p][c][f][m][unit]
+    return t, coef, np_(t.level).reshape(n_pairs, nc), np_(t.certificate)
+
+
+@pytest.mark.parametrize("name,K", [("D64", 6), ("D64", 4), ("PV2", 5)])
+def test_table_build_matches_oracle(name, K):
+    say(f"[table_build] {name} K={K}")
+    cfg = I.make_config(name)
+    m = cfg.model
+    P = m.n_species ** 2
+    model = B.Model.from_arrays(m, DEV)
+    _, coef, levels, cert = _gpu_table(model, P, K)
+    ref = _oracle_table(name, K)
+    worst_cert = [0.0, 0.0]
+    for p in range(P):
+        fn = TB.pair_chain(m, p)
+        lo, co = ref[p]
+        for c in range(1 << K):
+            dg, do = int(levels[p, c]), int(lo[c])
+            if dg != do:  # only where the estimates straddle the tolerance
+                e = TB.level_errors(fn, m.cutoff, K, c, min(dg, do))
+                assert abs(e - TB.TOL) <= 0.02 * TB.TOL, (p, c, dg, do, e)
+                continue
+            a_o = TB.power_form(co[c, : 1 << do])
+            a_g = coef[p, c, : 1 << do]
+            scale = np.abs(a_o).max(axis=1, keepdims=True)
+            assert np.all(np.abs(a_g - a_o) <= 3e-7 * scale), (p, c)
+        ev, ed = TB.certificate(levels[p], coef[p], fn, m.cutoff, K)
+        worst_cert = [max(worst_cert[0], ev), max(worst_cert[1], ed)]
+    np.testing.assert_allclose(cert, worst_cert, rtol=1e-3)
+    if K >= 5:
+        assert cert.max() <= 3e-7
+
+
+def _f32_chain(r, W1, W2, rc):
+    b = M.radial_basis(r, rc).astype(np.float32)
+    z1 = b @ W1
+    s1 = z1 / (np.float32(1) + np.exp(-z1))
+    z2 = s1 @ W2
+    return (z2 / (np.float32(1) + np.exp(-z2))).astype(np.float64)
+
+
+def _f32_table(levels, coef, r, rc, K):
+    """The stored table evaluated as the kernel does: float32 Horner in t."""
+    c, f, t, h = TB.locate(r, rc, K, levels)
+    out = np.zeros((len(r), coef.shape[-1]), np.float32)
+    tt = t.astype(np.float32)
+    for e in range(len(r)):
+        a = coef[c[e], f[e]].astype(np.float32)
+        v = a[-1].copy()
+        for q in range(a.shape[0] - 2, -1, -1):
+            v = (v * tt[e] + a[q]).astype(np.float32)
+        out[e] = v
+    return out.astype(np.float64)
+
+
+def test_table_more_accurate_than_float32_network():
+    cfg = I.make_config("D64")
+    m = cfg.model
+    K = 6
+    _, coef, levels, _ = _gpu_table(B.Model.from_arrays(m, DEV), 1, K)
+    r = np.random.default_rng(9).uniform(1.0, m.cutoff, 2000)
+    exact = TB.chain(r, m.W1[0], m.W2[0], m.cutoff)[0]
+    e_tab = np.abs(_f32_table(levels[0], coef[0], r, m.cutoff, K) - exact).max()
+    e_net = np.abs(_f32_chain(r, m.W1[0], m.W2[0], m.cutoff) - exact).max()
+    say(f"[table_vs_network] float32 table {e_tab:.3e}, float32 network {e_net:.3e}, ratio {e_tab / e_net:.3f}")
+    assert e_tab < e_net
+
+
+@pytest.mark.parametrize("name", ["D64", "D512", "D1728", "D64c128", "D512c128"])
+def test_energy_forces_tabulated(name):
+    say(f"[tabulated] {name}")
+    cfg = I.make_config(name)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    table = B.RadialTable(model, 6)
+    got = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, virial=True,
+                                                   variant="tabulated", table=table).items()}
+    ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
+    for k in ("energy", "atom_energy", "forces", "virial"):
+        assert np.all(np.isfinite(got[k])), k
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+    assert np.abs(got["virial"] - ref["virial"]).max() <= 1e-4 * np.abs(ref["virial"]).max()
+    # bit for bit repeatable
+    again = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, virial=True,
+                                                     variant="tabulated", table=table).items()}
+    for k in got:
+        np.testing.assert_array_equal(got[k], again[k])
+
+
+def test_tabulated_on_a_skin_list():
+    say("[tabulated] skin list D512")
+    cfg = I.make_config("D512")
+    pos0, species, model = device_inputs(cfg)
+    skin = 0.4
+    g = B.build_neighbors(pos0, cfg.box, cfg.model.cutoff + skin, species, 1)
+    d = np.random.default_rng(3).normal(size=cfg.pos.shape)
+    d *= (0.5 * skin) * np.random.default_rng(4).uniform(0.5, 1.0, (len(d), 1)) / np.linalg.norm(d, axis=1, keepdims=True)
+    moved = cfg.pos + d
+    got = {k: np_(v) for k, v in B.energy_forces(g, torch.as_tensor(moved).to(DEV), cfg.box, species, model,
+                                                   variant="tabulated", table=B.RadialTable(model, 6)).items()}
+    ref = M.energy_forces(I.wrap(moved, cfg.box), cfg.species, cfg.box, cfg.model)
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+
+
+def test_tabulated_takes_one_species():
+    cfg = I.make_config("PV2")
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    table = B.RadialTable(model, 4)
+    with pytest.raises(B.EECError) as ei:
+        B.energy_forces(g, pos, cfg.box, species, model, variant="tabulated", table=table)
+    assert ei.value.status == 2
