@@ -27,7 +27,11 @@ Also reported:
                 null when the kernel has changed since they were taken;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
                 (all receivers of the cell: their forward and force backward),
-                on the host cores.
+                on the host cores;
+  neighbors_ms  the neighbour build on its own (warm, preallocated buffers,
+                its host synchronisation included; the first, cold build as
+                neighbors_first_ms), and with_neighbours: a build followed by
+                the call, per step.
 """
 from __future__ import annotations
 
@@ -428,6 +432,29 @@ def main() -> int:
         kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
         return kernel, flop, launch_ms, flop / (launch_ms * 1e-3) / 1e12
 
+    # the neighbour build timed on its own (warm, into preallocated buffers,
+    # host synchronisation included), and build + call per step
+    nl = B.NeighborList(cfg.n_atoms, cfg.box, cfg.model.cutoff, E + 1024, dev, species, cfg.model.n_species)
+    ef_nb = B.EnergyForces(g, model, dev, atom_energy=True, variant=args.variant,
+                           table=table if args.variant == "tabulated" else None)
+    for _ in range(5):
+        nl.build(pos)
+    nb_times = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nl.build(pos)
+        torch.cuda.synchronize()
+        nb_times.append((time.perf_counter() - t0) * 1e3)
+    nb_warm_ms = float(np.median(nb_times))
+    n_with = max(args.steps // 4, 10)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_with):
+        ef_nb(pos, cfg.box, species, graph=nl.build(pos))
+    torch.cuda.synchronize()
+    with_ms = (time.perf_counter() - t0) * 1e3 / n_with
+
     kernel, flop, launch_ms, achieved = roof(args.variant, dom_ms)
     out = {
         "metric": METRIC,
@@ -457,7 +484,9 @@ def main() -> int:
                     **({"table_certificate": cert, "approximate": True} if other == "tabulated" else {})}
             for other, (o_ms, o_phase, o_energy, o_dom) in other_res.items()},
         "phases_ms": phase_ms,
-        "neighbors_ms": nb_ms,
+        "neighbors_ms": nb_warm_ms,
+        "neighbors_first_ms": nb_ms,
+        "with_neighbours": {"ms_per_step": with_ms, "value": E / (with_ms * 1e-3), "steps": n_with},
         "energy": energy,
     }
     if not args.no_cpu_baseline:
