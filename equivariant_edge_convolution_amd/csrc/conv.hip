@@ -408,21 +408,42 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
 #pragma unroll
   for (int k = 0; k < 9; ++k) v[k] = 0.0;
   const int a = rp[i], b = rp[i + 1];
-  for (int e = a + lane; e < b; e += 64) {
-    const int er = min(max(rev[e], 0), (int)E - 1);
-    const float gx = g[3 * e], gy = g[3 * e + 1], gz = g[3 * e + 2];
-    fx += gx - g[3 * er];
-    fy += gy - g[3 * er + 1];
-    fz += gz - g[3 * er + 2];
-    if (VIRIAL) {
-      const int j = min(max(col[e], 0), n - 1);
-      double d[3];
-      edge_vector(pos, i, j, shift + 3 * e, Lx, Ly, Lz, d);
-      const double gg[3] = {gx, gy, gz};
+  // Four 64-edge chunks per pass: every reverse index, then every gradient
+  // row, is loaded before the sums, which run edge by edge in the same order
+  // as one chunk at a time would.
+  constexpr int U = 4;
+  for (int e0 = a + lane; e0 < b; e0 += 64 * U) {
+    int er[U];
+    float ge[U][3], gr[U][3];
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
+    for (int u = 0; u < U; ++u) er[u] = e0 + 64 * u < b ? min(max(rev[e0 + 64 * u], 0), (int)E - 1) : 0;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) v[3 * p + q] -= d[p] * gg[q];
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + 64 * u;
+      const bool ok = e < b;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        ge[u][q] = ok ? g[3 * e + q] : 0.f;
+        gr[u][q] = ok ? g[3 * er[u] + q] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + 64 * u;
+      if (e >= b) break;
+      fx += ge[u][0] - gr[u][0];
+      fy += ge[u][1] - gr[u][1];
+      fz += ge[u][2] - gr[u][2];
+      if (VIRIAL) {
+        const int j = min(max(col[e], 0), n - 1);
+        double d[3];
+        edge_vector(pos, i, j, shift + 3 * e, Lx, Ly, Lz, d);
+        const double gg[3] = {ge[u][0], ge[u][1], ge[u][2]};
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int q = 0; q < 3; ++q) v[3 * p + q] -= d[p] * gg[q];
+      }
     }
   }
   for (int off = 32; off > 0; off >>= 1) {

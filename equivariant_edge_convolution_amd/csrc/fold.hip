@@ -955,6 +955,63 @@ __device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, c
   wave_sync_lds();
 }
 
+// Few receivers: a workgroup per receiver, its W waves sharing the row's tiles
+// (as k_fold_split), s2 and ds2/dr from the radial table.
+template <int C, int W>
+__global__ void __launch_bounds__(64 * W)
+k_fold_split_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float* __restrict__ ei,
+                   float* __restrict__ gout, float* __restrict__ stash) {
+  __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
+  __shared__ __align__(16) float msh[NLM][HID + 1];  // M of the receiver, read by every wave
+  __shared__ float4 tpb[W][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const WaveLds<C> L(wbuf[wave]);
+  const int N = un.n_atoms;
+  float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+  for (int i = blockIdx.x; i < N; i += gridDim.x) {
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
+    const Recv xi = recv_pos(in, i);
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
+    int j = 0;
+    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
+      fwd_tile_tab(in, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T,
+                   j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
+    __syncthreads();
+    if (wave == 0) {
+      // T = sum of the waves' partials, in wave order (lane: 16 consecutive entries)
+      float* tw = &L.tsm[0][0];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = tw[16 * lane + e];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += wbuf[w][FoldLds<C>::TSM + 16 * lane + e];
+        tw[16 * lane + e] = v;
+      }
+      wave_sync_lds();
+      float macc[NLM];
+      const float* gl = G + lane;
+      const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return gl[(l * HID + kk) * HID]; }, macc);
+      if (lane == 0) ei[i] = e2;
+#pragma unroll
+      for (int lm = 0; lm < NLM; ++lm) msh[lm][lane] = macc[lm];
+    }
+    __syncthreads();
+    j = 0;
+    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
+      bwd_tile_tab(in, xi, ta, msh, L.ybsm, q0, qa, qb, s, h, gout,
+                   j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+    __syncthreads();  // msh and the wave buffers are rewritten for the next receiver
+  }
+}
+
 template <int C, int W>
 __global__ void __launch_bounds__(64 * W)
 k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float* __restrict__ ei,
@@ -1208,10 +1265,16 @@ void launch_fold_table(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
   ta.level = level;
   ta.n_coarse = 1 << log2_pieces;
   ta.inv_h0 = (double)ta.n_coarse / m->cutoff;
-  if (p.C == 64)
+  if (use_split(p)) {
+    if (p.C == 64)
+      k_fold_split_table<64, WAVES><<<split_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
+    else
+      k_fold_split_table<128, WAVES><<<split_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
+  } else if (p.C == 64) {
     k_fold_table<64, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
-  else
+  } else {
     k_fold_table<128, WAVES><<<unit_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
+  }
 }
 
 size_t fold_stash_bytes(const ConvPlan& p) {
