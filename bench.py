@@ -336,7 +336,7 @@ def main() -> int:
                     help="direct: the radial weights R of every edge (eec_energy_forces); folded: the "
                          "last radial layer moved past the edge sum (eec_energy_forces_folded); "
                          "tabulated: s2 and ds2/dr from certified radial tables "
-                         "(eec_energy_forces_tabulated, approximate, one species)")
+                         "(eec_energy_forces_tabulated, approximate, one to three species)")
     ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy", "md"],
                     help="energy_forces: the headline call; edge_message: the chunked streaming "
                          "forward (radial rows + message pass), for profiling its kernels; copy: a "
@@ -417,7 +417,7 @@ def main() -> int:
         return dt * 1e3 / steps, phase_ms, float(ef.energy.cpu()[0]), dom_ms
 
     table = None
-    if args.variant == "tabulated" or (cfg.model.n_species == 1 and not args.no_other_variant):
+    if args.variant == "tabulated" or (cfg.model.n_species <= 3 and not args.no_other_variant):
         table = B.RadialTable(model, 6)
         cert = [float(x) for x in table.certificate.cpu()]
     ms_per_step, phase_ms, energy, dom_ms = timed(args.variant, args.steps, args.warmup)

@@ -264,7 +264,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
       return fail(EEC_ERR_NULL, "radial table is NULL");
     if (tab->log2_pieces < TAB_MIN_LOG2 || tab->log2_pieces > TAB_MAX_LOG2)
       return fail(EEC_ERR_SHAPE, "radial table log2_pieces out of range");
-    if (m->n_species != 1) return fail(EEC_ERR_SHAPE, "the tabulated variant takes one species");
+    if (m->n_species > 3) return fail(EEC_ERR_SHAPE, "the tabulated variant takes one to three species");
     if (((uintptr_t)tab->coef & 7) != 0) return fail(EEC_ERR_SHAPE, "radial table must be 8-byte aligned");
   }
   const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
@@ -294,12 +294,21 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   float* gbuf = (float*)(ws + p.off_g);
   const bool folded = variant == EEC_VARIANT_FOLDED;
   if (tabulated) {
-    // one kernel per receiver, s2 and ds2/dr from the radial table
+    // one kernel per receiver, s2 and ds2/dr from the radial tables
     mark(2 * EEC_PHASE_PREPARE);
-    launch_gram(s, p, m, ws);
+    if (p.S == 1) {
+      launch_gram(s, p, m, ws);
+    } else {
+      launch_prepare_rows(s, p, g, species, ws);
+      launch_transpose_w3(s, p, m, ws);
+    }
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);
-    launch_fold_table(s, p, g, pos, b, m->cutoff, m, tab->log2_pieces, tab->coef, tab->level, ei, gbuf, ws);
+    if (p.S == 1)
+      launch_fold_table(s, p, g, pos, b, m->cutoff, m, tab->log2_pieces, tab->coef, tab->level, ei, gbuf, ws);
+    else
+      launch_fold_multi(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws, tab->log2_pieces, tab->coef,
+                        tab->level);
     mark(2 * EEC_PHASE_FORWARD + 1);
     for (int k : {EEC_PHASE_READOUT, EEC_PHASE_BACKWARD}) {
       mark(2 * k);

@@ -130,12 +130,14 @@ void launch_fold_fused(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
                        char* ws);
 
 // Two or three species: the whole folded call per receiver in one kernel,
-// sender species after sender species (needs launch_prepare,
-// launch_species_order and launch_transpose_w3 first on the stream).
+// sender species after sender species (needs launch_prepare_rows and
+// launch_transpose_w3 first on the stream).  With `tab` (a radial table set of
+// 2^log2_pieces coarse pieces, levels `level`), s2 and ds2/dr come from it.
 bool fold_multi_supported(const ConvPlan& p);
 void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
-                       char* ws);
+                       char* ws, int log2_pieces = 0, const float* tab = nullptr,
+                       const int32_t* level = nullptr);
 
 // Radial tables (one species pair after another): polynomials of degree
 // TAB_DEG on the 2^d(c) sub-pieces of each of 2^log2_pieces coarse pieces of

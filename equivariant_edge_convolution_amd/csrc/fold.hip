@@ -723,6 +723,14 @@ struct TabArgs {
   int n_coarse;
 };
 
+// The slice of a table set that belongs to species pair p.
+__device__ __forceinline__ TabArgs tab_pair(const TabArgs& ta, int p) {
+  TabArgs t = ta;
+  t.tab += (size_t)p * ta.n_coarse * TAB_SUB * TAB_NC * 32;
+  t.level += (size_t)p * ta.n_coarse;
+  return t;
+}
+
 // Sub-piece and local variable of an edge at distance r (binary64, then
 // float32): u = r / h0, coarse c = floor(u), w = (u - c) 2^d(c), f = floor(w),
 // t = 2 (w - f) - 1 in [-1, 1), dt/dr = 2^(d+1) / h0.  Returned as (t, slot
@@ -756,11 +764,11 @@ __device__ __forceinline__ void tab_horner(const float2* __restrict__ c, float t
   }
 }
 
-__device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const Recv& xi, const TabArgs& ta, float4* tp,
-                                             float (*ysm)[NLM + 1], int q0, int qa, int qb, int s, int h,
-                                             f32x4 T[4], float* zs) {
+__device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const int32_t* perm, const Recv& xi,
+                                             const TabArgs& ta, float4* tp, float (*ysm)[NLM + 1], int q0, int qa,
+                                             int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
-  const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(nullptr, q0, qa, qb, s)), xi.x);
+  const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
   if (zs != nullptr && valid && h == 0) {
     float* row = zs + s * ZROW + 2 * HID;
     float rw[2];
@@ -844,11 +852,12 @@ __device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const Recv& xi, c
   wave_sync_lds();
 }
 
-__device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, const TabArgs& ta,
-                                             float (*msm)[HID + 1], float (*ybsm)[NLM + 1], int q0, int qa,
-                                             int qb, int s, int h, float* __restrict__ gout, const float* zs) {
+__device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, const int32_t* perm,
+                                             const TabArgs& ta, float (*msm)[HID + 1], float (*ybsm)[NLM + 1],
+                                             int q0, int qa, int qb, int s, int h, float* __restrict__ gout,
+                                             const float* zs) {
   const bool valid = q0 + s < qb;
-  const int64_t e = tile_edge(nullptr, q0, qa, qb, s);
+  const int64_t e = tile_edge(perm, q0, qa, qb, s);
   Geo g;
   f32x16 ds[2], s2[2];  // ds2/dr and s2, edges on N: register 4j + i of tile m = hidden 4h + 32m + 8j + i
   if (zs != nullptr) {
@@ -978,7 +987,7 @@ k_fold_split_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G,
     for (int b = 0; b < 4; ++b) T[b] = zero4();
     int j = 0;
     for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      fwd_tile_tab(in, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T,
+      fwd_tile_tab(in, nullptr, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T,
                    j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -1006,7 +1015,7 @@ k_fold_split_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G,
     __syncthreads();
     j = 0;
     for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      bwd_tile_tab(in, xi, ta, msh, L.ybsm, q0, qa, qb, s, h, gout,
+      bwd_tile_tab(in, xi, nullptr, ta, msh, L.ybsm, q0, qa, qb, s, h, gout,
                    j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
     __syncthreads();  // msh and the wave buffers are rewritten for the next receiver
   }
@@ -1037,7 +1046,7 @@ k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float
     const Recv xi = recv_pos(in, i);
     float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
     for (int q0 = qa; q0 < qb; q0 += 32)
-      fwd_tile_tab(in, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
+      fwd_tile_tab(in, nullptr, xi, ta, tpb[wave], L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -1053,7 +1062,7 @@ k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float
     for (int lm = 0; lm < NLM; ++lm) L.msm[lm][lane] = macc[lm];
     wave_sync_lds();
     for (int q0 = qa; q0 < qb; q0 += 32)
-      bwd_tile_tab(in, xi, ta, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
+      bwd_tile_tab(in, xi, nullptr, ta, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
   }
 }
 
@@ -1076,15 +1085,18 @@ struct MultiLds {
   static constexpr int WEIGHTS = W3L ? Lds<C>::FLOATS : W12_FLOATS;
 };
 
-template <int C, int W, bool W3L>
+// TAB: s2 and ds2/dr of each sender species' pair from the radial tables (only
+// W3 is staged); otherwise from the network.
+template <int C, int W, bool W3L, bool TAB>
 __global__ void __launch_bounds__(64 * W)
 k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t* __restrict__ zstart,
              const float* __restrict__ W1, const float* __restrict__ W2, const float* __restrict__ W3,
              const float* __restrict__ W3T, const float* __restrict__ emb, const float* __restrict__ w_read,
-             float* __restrict__ ei, float* __restrict__ gout, float* __restrict__ stash) {
+             TabArgs ta, float* __restrict__ ei, float* __restrict__ gout, float* __restrict__ stash) {
   constexpr int NC = 4 * C, CPL = C / 64;
   __shared__ float wl[MultiLds<C, W3L>::WEIGHTS];
   __shared__ __align__(16) float wbuf[W][MultiLds<C, W3L>::PW];
+  __shared__ float4 tpb[W][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
   const float* w1s = wl + Lds<C>::W1;
@@ -1099,8 +1111,11 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
   const int total = bstart[MULTI_MAX_S];
   float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
   auto stage = [&](int p) {
+    if (TAB && !W3L) return;  // nothing to stage
     __syncthreads();
-    if (W3L)
+    if (TAB)
+      stage_rows(wl + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
+    else if (W3L)
       stage_weights<C>(wl, W1, W2, W3, p);
     else
       stage_w12(wl, W1, W2, p);
@@ -1132,9 +1147,13 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
       f32x4 T[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) T[bb] = zero4();
-      for (int q0 = qa; q0 < qb; q0 += 32, ++t)
-        fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
-                 t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr);
+      for (int q0 = qa; q0 < qb; q0 += 32, ++t) {
+        float* zs = t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr;
+        if (TAB)
+          fwd_tile_tab(in, un.perm, xi, tab_pair(ta, p), tpb[wave], L.ysm, q0, qa, qb, s, h, T, zs);
+        else
+          fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, zs);
+      }
       float as[CPL][NLM];
       if (W3L)
         unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, as);
@@ -1186,9 +1205,13 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
         unit_M<C, 1>(L.ahsm, wl + Lds<C>::W3 + lane * Lds<C>::LD3, lane, L.msm);
       else
         unit_M<C, HID>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
-      for (int q0 = qa; q0 < qb; q0 += 32, ++t)
-        bwd_tile(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout,
-                 t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr);
+      for (int q0 = qa; q0 < qb; q0 += 32, ++t) {
+        const float* zs = t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr;
+        if (TAB)
+          bwd_tile_tab(in, xi, un.perm, tab_pair(ta, p), L.msm, L.ybsm, q0, qa, qb, s, h, gout, zs);
+        else
+          bwd_tile(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, zs);
+      }
     }
   }
 }
@@ -1233,6 +1256,15 @@ Units make_units(const ConvPlan& p, const eec_graph* g, const int32_t* species, 
   return un;
 }
 
+TabArgs tab_args(const eec_model* m, int log2_pieces, const float* tab, const int32_t* level) {
+  TabArgs ta;
+  ta.tab = reinterpret_cast<const float2*>(tab);
+  ta.level = level;
+  ta.n_coarse = 1 << log2_pieces;
+  ta.inv_h0 = (double)ta.n_coarse / m->cutoff;
+  return ta;
+}
+
 int unit_grid(const ConvPlan& p) {
   const int64_t batches = (int64_t)p.P * ((p.N + WAVES - 1) / WAVES);
   return (int)std::max<int64_t>(1, std::min<int64_t>(batches, 256));
@@ -1260,11 +1292,7 @@ void launch_fold_table(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
   float* stash = (float*)(ws + p.off_stash);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, nullptr);
   const Units un = make_units(p, g, nullptr, ws);
-  TabArgs ta;
-  ta.tab = reinterpret_cast<const float2*>(tab);
-  ta.level = level;
-  ta.n_coarse = 1 << log2_pieces;
-  ta.inv_h0 = (double)ta.n_coarse / m->cutoff;
+  const TabArgs ta = tab_args(m, log2_pieces, tab, level);
   if (use_split(p)) {
     if (p.C == 64)
       k_fold_split_table<64, WAVES><<<split_grid(p), 64 * WAVES, 0, s>>>(in, un, ta, G, ei, gout, stash);
@@ -1286,7 +1314,7 @@ size_t fold_stash_bytes(const ConvPlan& p) {
 
 void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos, Box box,
                        double cutoff, const int32_t* species, const eec_model* m, float* ei, float* gout,
-                       char* ws) {
+                       char* ws, int log2_pieces, const float* tab, const int32_t* level) {
   if (p.N == 0) return;
   const float* W3T = (const float*)(ws + p.off_w3t);
   float* stash = (float*)(ws + p.off_stash);
@@ -1294,12 +1322,20 @@ void launch_fold_multi(hipStream_t s, const ConvPlan& p, const eec_graph* g, con
   const int32_t* zstart = (const int32_t*)(ws + p.off_zstart);
   const EdgeIn in = make_in_f(p, g, pos, box, cutoff, species);
   const Units un = make_units(p, g, species, ws);
-  if (p.C == 64)
-    k_fold_multi<64, WAVES, true><<<multi_grid(p), 64 * WAVES, 0, s>>>(in, un, ord, zstart, m->W1, m->W2, m->W3,
-                                                                        W3T, m->emb, m->w_read, ei, gout, stash);
+  const TabArgs ta = tab_args(m, log2_pieces, tab, level);
+  const bool t = tab != nullptr;
+  if (p.C == 64 && t)
+    k_fold_multi<64, WAVES, true, true><<<multi_grid(p), 64 * WAVES, 0, s>>>(
+        in, un, ord, zstart, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ta, ei, gout, stash);
+  else if (p.C == 64)
+    k_fold_multi<64, WAVES, true, false><<<multi_grid(p), 64 * WAVES, 0, s>>>(
+        in, un, ord, zstart, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ta, ei, gout, stash);
+  else if (t)
+    k_fold_multi<128, WAVES, false, true><<<multi_grid(p), 64 * WAVES, 0, s>>>(
+        in, un, ord, zstart, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ta, ei, gout, stash);
   else
-    k_fold_multi<128, WAVES, false><<<multi_grid(p), 64 * WAVES, 0, s>>>(in, un, ord, zstart, m->W1, m->W2, m->W3,
-                                                                          W3T, m->emb, m->w_read, ei, gout, stash);
+    k_fold_multi<128, WAVES, false, false><<<multi_grid(p), 64 * WAVES, 0, s>>>(
+        in, un, ord, zstart, m->W1, m->W2, m->W3, W3T, m->emb, m->w_read, ta, ei, gout, stash);
 }
 
 void launch_fold_forward(hipStream_t s, const ConvPlan& p, const eec_graph* g, const double* pos,

@@ -302,13 +302,13 @@ EEC_API eec_status eec_radial_table_build(void *stream, const eec_model *m, int3
                                   float *coef, size_t coef_floats, int32_t *level,
                                   double *certificate);
 
-/* eec_energy_forces_tabulated -- the outputs of eec_energy_forces_folded, one
- * species, with s2 and ds2/dr of every edge read from `tab` (built for this
- * model) instead of the basis and the first two layers: per edge a Horner
- * evaluation of 64 units and their derivatives replaces two dense layers and
- * their SiLUs in both passes.  Edges at or beyond the cutoff add exactly zero.
- * Arguments as eec_energy_forces; same workspace size.  EEC_ERR_SHAPE for
- * more than one species. */
+/* eec_energy_forces_tabulated -- the outputs of eec_energy_forces_folded, with
+ * s2 and ds2/dr of every edge read from the table of its species pair in
+ * `tab` (built for this model) instead of the basis and the first two layers:
+ * per edge a Horner evaluation of 64 units and their derivatives replaces two
+ * dense layers and their SiLUs in both passes.  Edges at or beyond the cutoff
+ * add exactly zero.  Arguments as eec_energy_forces; same workspace size.
+ * One to three species (EEC_ERR_SHAPE for four). */
 EEC_API eec_status eec_energy_forces_tabulated(void *stream, const eec_graph *g, const double *pos,
                                        const double *box /*[host][3]*/, const int32_t *species,
                                        const eec_model *m, const eec_radial_table *tab,

@@ -132,7 +132,7 @@ def test_radial_table_host_side_errors():
     args = (None, ctypes.byref(g), vp(1 << 16), box, vp(1 << 17), ctypes.byref(m))
     outs = (vp(1 << 25), None, vp(1 << 26), None, vp(1 << 28), 1 << 24)
     assert B.STATUS[L.eec_energy_forces_tabulated(*args, None, *outs)] == "EEC_ERR_NULL"
-    m3 = _model_struct(n_species=3, fake_ptr=1 << 20)
+    m3 = _model_struct(n_species=4, fake_ptr=1 << 20)
     t = B._Table(6, 1 << 29, 1 << 30)
     args3 = (None, ctypes.byref(g), vp(1 << 16), box, vp(1 << 17), ctypes.byref(m3))
     assert B.STATUS[L.eec_energy_forces_tabulated(*args3, ctypes.byref(t), *outs)] == "EEC_ERR_SHAPE"

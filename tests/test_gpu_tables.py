@@ -107,7 +107,7 @@ def test_table_more_accurate_than_float32_network():
     assert e_tab < e_net
 
 
-@pytest.mark.parametrize("name", ["D64", "D512", "D1728", "D64c128", "D512c128"])
+@pytest.mark.parametrize("name", ["D64", "D512", "D1728", "D64c128", "D512c128", "RS2", "RS3", "PV2", "PV3"])
 def test_energy_forces_tabulated(name):
     say(f"[tabulated] {name}")
     cfg = I.make_config(name)
@@ -146,8 +146,10 @@ def test_tabulated_on_a_skin_list():
     assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
 
 
-def test_tabulated_takes_one_species():
-    cfg = I.make_config("PV2")
+def test_tabulated_takes_at_most_three_species():
+    rng = np.random.default_rng(8)
+    box = np.array([14.0, 14.0, 14.0])
+    cfg = I.make_cluster(rng.uniform(0.0, 14.0, (24, 3)), box, species=np.arange(24) % 4, n_species=4)
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
     table = B.RadialTable(model, 4)
