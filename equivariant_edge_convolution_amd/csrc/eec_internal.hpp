@@ -25,7 +25,7 @@ struct NbPlan {
   int64_t n_cells;
   size_t bytes;
   // byte offsets into the workspace
-  size_t off_cell_count, off_cell_fill, off_cell_start, off_cell_atoms, off_cell_of, off_deg,
+  size_t off_cell_count, off_cell_fill, off_cell_start, off_cell_atoms, off_cell_of, off_cell_pos, off_deg,
       off_scratch;
 };
 NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff);

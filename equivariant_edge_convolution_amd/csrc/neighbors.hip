@@ -30,6 +30,28 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     p[k] = v;
 }
 
+// counters[c] += 1 for every active lane, one atomic per distinct c in the
+// wave; returns the lane's slot (the counter's old value plus its rank among
+// the lanes with the same c).  Slots within a cell depend on the order the
+// waves arrive in; the rows are sorted afterwards, so the output does not.
+__device__ __forceinline__ uint32_t wave_count(uint32_t* __restrict__ counters, int c) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t pending = __ballot(1);
+  uint32_t slot = 0;
+  while (pending != 0ull) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int c0 = __shfl(c, leader);
+    const uint64_t same = __ballot(c == c0) & pending;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(&counters[c0], (uint32_t)__popcll(same));
+    base = __shfl(base, leader);
+    if ((same >> lane) & 1ull) slot = base + (uint32_t)__popcll(same & below);
+    pending &= ~same;
+  }
+  return slot;
+}
+
 __global__ void k_nb_bin(int32_t n, const double* __restrict__ pos, double Lx, double Ly, double Lz,
                          int nc0, int nc1, int nc2, const int32_t* __restrict__ species,
                          int32_t n_species, int32_t* __restrict__ cell_of,
@@ -53,7 +75,7 @@ __global__ void k_nb_bin(int32_t n, const double* __restrict__ pos, double Lx, d
     if (zs < 0 || zs >= n_species) atomicOr(flags, FLAG_SPECIES);
   }
   cell_of[i] = c;
-  atomicAdd(&cell_count[c], 1u);
+  wave_count(cell_count, c);
 }
 
 // Exclusive scan of n unsigned counts into out[0..n] (out[n] = total) with one
@@ -87,14 +109,20 @@ __global__ void __launch_bounds__(1024) k_scan_excl(const uint32_t* __restrict__
   }
 }
 
-__global__ void k_cell_place(int32_t n, const int32_t* __restrict__ cell_of,
+// Atom i into the next slot of its cell, and its position into the same slot
+// of the cell-ordered copy (read contiguously by the candidate scans).
+__global__ void k_cell_place(int32_t n, const double* __restrict__ pos, const int32_t* __restrict__ cell_of,
                              const int32_t* __restrict__ cell_start,
-                             uint32_t* __restrict__ cell_fill, int32_t* __restrict__ cell_atoms) {
+                             uint32_t* __restrict__ cell_fill, int32_t* __restrict__ cell_atoms,
+                             double* __restrict__ cell_pos) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int c = cell_of[i];
-  const uint32_t slot = atomicAdd(&cell_fill[c], 1u);
-  cell_atoms[cell_start[c] + slot] = i;
+  const uint32_t slot = wave_count(cell_fill, c);
+  const int k = cell_start[c] + slot;
+  cell_atoms[k] = i;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) cell_pos[3 * k + q] = pos[3 * i + q];
 }
 
 struct Grid {
@@ -108,29 +136,80 @@ template <class F>
 __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const double* __restrict__ pos,
                                                const int32_t* __restrict__ cell_of,
                                                const int32_t* __restrict__ cell_start,
-                                               const int32_t* __restrict__ cell_atoms, int lane,
+                                               const int32_t* __restrict__ cell_atoms,
+                                               const double* __restrict__ cell_pos, int nmax, int lane,
                                                F&& f) {
-  const int ci = cell_of[i];
+  // i is the wave's receiver: its cell and the candidate cells' ranges are
+  // wave-uniform and come through the scalar unit
+  i = __builtin_amdgcn_readfirstlane(i);
+  const int ci = __builtin_amdgcn_readfirstlane(cell_of[i]);
   const int cz = ci % gr.nc2, cy = (ci / gr.nc2) % gr.nc1, cx = ci / (gr.nc2 * gr.nc1);
-  for (int o = 0; o < 27; ++o) {
+  const double xi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+  auto cell = [&](int o, int& c2, int& s, int sh[3]) {
     const int vx = cx + o / 9 - 1, vy = cy + (o / 3) % 3 - 1, vz = cz + o % 3 - 1;
-    const int ix = vx < 0 ? -1 : (vx >= gr.nc0 ? 1 : 0);
-    const int iy = vy < 0 ? -1 : (vy >= gr.nc1 ? 1 : 0);
-    const int iz = vz < 0 ? -1 : (vz >= gr.nc2 ? 1 : 0);
-    const int wx = vx - ix * gr.nc0, wy = vy - iy * gr.nc1, wz = vz - iz * gr.nc2;
-    const int c2 = (wx * gr.nc1 + wy) * gr.nc2 + wz;
-    const int s = (ix + 1) * 9 + (iy + 1) * 3 + (iz + 1);
+    sh[0] = vx < 0 ? -1 : (vx >= gr.nc0 ? 1 : 0);
+    sh[1] = vy < 0 ? -1 : (vy >= gr.nc1 ? 1 : 0);
+    sh[2] = vz < 0 ? -1 : (vz >= gr.nc2 ? 1 : 0);
+    const int wx = vx - sh[0] * gr.nc0, wy = vy - sh[1] * gr.nc1, wz = vz - sh[2] * gr.nc2;
+    c2 = (wx * gr.nc1 + wy) * gr.nc2 + wz;
+    s = (sh[0] + 1) * 9 + (sh[1] + 1) * 3 + (sh[2] + 1);
+  };
+  // The first 64 members of three cells at a time, every load issued before
+  // the tests; d = (x_j - x_i) + n L in binary64 as edge_vector forms it.
+  constexpr int G = 3;
+  for (int o0 = 0; o0 < 27; o0 += G) {
+    int c2[G], s[G], sh[G][3], a[G], b[G], j[G];
+    double xj[G][3];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      cell(o0 + u, c2[u], s[u], sh[u]);
+      c2[u] = __builtin_amdgcn_readfirstlane(c2[u]);
+      a[u] = cell_start[c2[u]];
+      b[u] = cell_start[c2[u] + 1];
+    }
+    // loads from a valid slot in every lane (no load under a branch); lanes
+    // past the cell's end are masked out below
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int k = min(a[u] + lane < b[u] ? a[u] + lane : a[u], nmax);
+      j[u] = cell_atoms[k];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) xj[u][q] = cell_pos[3 * k + q];
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const bool in_cell = a[u] + lane < b[u];
+      if (!in_cell) j[u] = i;
+      const double L[3] = {gr.Lx, gr.Ly, gr.Lz};
+      double d[3];
+      {
+#pragma clang fp contract(off)
+        for (int q = 0; q < 3; ++q) d[q] = (xj[u][q] - xi[q]) + (double)(int8_t)sh[u][q] * L[q];
+      }
+      const double r2 = norm2_nofma(d);
+      const bool keep = in_cell && (r2 < gr.rc2) && !(j[u] == i && s[u] == 13);
+      f(keep, j[u], s[u], in_cell ? r2 : 1.0);
+    }
+  }
+  // members past the first 64 of a cell
+  for (int o = 0; o < 27; ++o) {
+    int c2, s, shv[3];
+    cell(o, c2, s, shv);
+    const int ix = shv[0], iy = shv[1], iz = shv[2];
     const int a = cell_start[c2], b = cell_start[c2 + 1];
-    for (int base = a; base < b; base += 64) {
+    for (int base = a + 64; base < b; base += 64) {
       const int k = base + lane;
       bool keep = false;
       int j = 0;
       double r2 = 1.0;
       if (k < b) {
         j = cell_atoms[k];
-        int8_t sh[3] = {(int8_t)ix, (int8_t)iy, (int8_t)iz};
+        const double L[3] = {gr.Lx, gr.Ly, gr.Lz}, shd[3] = {(double)ix, (double)iy, (double)iz};
         double d[3];
-        edge_vector(pos, i, j, sh, gr.Lx, gr.Ly, gr.Lz, d);
+        {
+#pragma clang fp contract(off)
+          for (int q = 0; q < 3; ++q) d[q] = (cell_pos[3 * k + q] - xi[q]) + shd[q] * L[q];
+        }
         r2 = norm2_nofma(d);
         keep = (r2 < gr.rc2) && !(j == i && s == 13);
       }
@@ -143,6 +222,7 @@ __global__ void __launch_bounds__(256) k_nb_count(int32_t n, Grid gr, const doub
                                                   const int32_t* __restrict__ cell_of,
                                                   const int32_t* __restrict__ cell_start,
                                                   const int32_t* __restrict__ cell_atoms,
+                                                  const double* __restrict__ cell_pos,
                                                   uint32_t* __restrict__ deg,
                                                   uint32_t* __restrict__ flags) {
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -150,7 +230,7 @@ __global__ void __launch_bounds__(256) k_nb_count(int32_t n, Grid gr, const doub
   if (i >= n) return;
   uint32_t cnt = 0;
   bool coincident = false;
-  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, lane,
+  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, n - 1, lane,
                  [&](bool keep, int, int, double r2) {
                    cnt += keep ? 1u : 0u;
                    coincident |= keep && (r2 == 0.0);
@@ -165,6 +245,7 @@ __global__ void __launch_bounds__(256) k_nb_fill(int32_t n, Grid gr, const doubl
                                                  const int32_t* __restrict__ cell_of,
                                                  const int32_t* __restrict__ cell_start,
                                                  const int32_t* __restrict__ cell_atoms,
+                                                 const double* __restrict__ cell_pos,
                                                  const int32_t* __restrict__ rp,
                                                  int32_t* __restrict__ keys) {
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -173,7 +254,7 @@ __global__ void __launch_bounds__(256) k_nb_fill(int32_t n, Grid gr, const doubl
   int base = rp[i];
   const int end = rp[i + 1];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, lane,
+  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, n - 1, lane,
                  [&](bool keep, int j, int s, double) {
                    const uint64_t mask = __ballot(keep);
                    const int at = base + __popcll(mask & below);
@@ -192,20 +273,44 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
   const int lane = threadIdx.x;
   if (i >= n) return;
   const int a = rp[i], deg = rp[i + 1] - a;
-  const bool in_lds = deg <= SORT_LDS;
-  if (in_lds)
-    for (int k = lane; k < deg; k += 64) sk[k] = keys[a + k];
-  __syncthreads();
-  const int32_t* src = in_lds ? sk : keys + a;
-  for (int k = lane; k < deg; k += 64) {
-    const int32_t key = src[k];
-    int rank = 0;
-    for (int q = 0; q < deg; ++q) rank += (src[q] < key) ? 1 : 0;
+  auto emit = [&](int r, int32_t key) {
     const int s = key % 27;
-    col[a + rank] = key / 27;
-    shift[3 * (a + rank) + 0] = (int8_t)(s / 9 - 1);
-    shift[3 * (a + rank) + 1] = (int8_t)((s / 3) % 3 - 1);
-    shift[3 * (a + rank) + 2] = (int8_t)(s % 3 - 1);
+    col[a + r] = key / 27;
+    shift[3 * (a + r) + 0] = (int8_t)(s / 9 - 1);
+    shift[3 * (a + r) + 1] = (int8_t)((s / 3) % 3 - 1);
+    shift[3 * (a + r) + 2] = (int8_t)(s % 3 - 1);
+  };
+  if (deg <= SORT_LDS) {
+    // bitonic sort of the keys padded to a power of two (the pads sort last)
+    int np2 = 64;
+    while (np2 < deg) np2 <<= 1;
+    for (int k = lane; k < np2; k += 64) sk[k] = k < deg ? keys[a + k] : INT32_MAX;
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int x = lane; x < np2; x += 64) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const int32_t kx = sk[x], ky = sk[y];
+            const bool up = (x & k) == 0;
+            if ((kx > ky) == up) {
+              sk[x] = ky;
+              sk[y] = kx;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int k = lane; k < deg; k += 64) emit(k, sk[k]);
+  } else {
+    const int32_t* src = keys + a;
+    for (int k = lane; k < deg; k += 64) {
+      const int32_t key = src[k];
+      int rank = 0;
+      for (int q = 0; q < deg; ++q) rank += (src[q] < key) ? 1 : 0;
+      emit(rank, key);
+    }
   }
 }
 
@@ -227,12 +332,16 @@ __global__ void __launch_bounds__(256) k_nb_rev(int32_t n, const int32_t* __rest
     const int j = col[e];
     const int s = (shift[3 * e] + 1) * 9 + (shift[3 * e + 1] + 1) * 3 + (shift[3 * e + 2] + 1);
     const int32_t target = i * 27 + (26 - s);
-    int lo = rp[j], hi = rp[j + 1];
+    // first entry of row j with sender i (rows are sorted by sender, then
+    // image), then the image among those
+    const int end = rp[j + 1];
+    int lo = rp[j], hi = end;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (key_at(col, shift, mid) < target) lo = mid + 1; else hi = mid;
+      if (col[mid] < i) lo = mid + 1; else hi = mid;
     }
-    if (lo < rp[j + 1] && key_at(col, shift, lo) == target) {
+    while (lo < end && col[lo] == i && key_at(col, shift, lo) < target) ++lo;
+    if (lo < end && key_at(col, shift, lo) == target) {
       rev[e] = lo;
     } else {
       rev[e] = e;
@@ -321,6 +430,7 @@ NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff) {
   p.off_cell_start = o; o += align256(sizeof(int32_t) * (p.n_cells + 1));
   p.off_cell_atoms = o; o += align256(sizeof(int32_t) * std::max<int64_t>(N, 1));
   p.off_cell_of = o;    o += align256(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  p.off_cell_pos = o;   o += align256(3 * sizeof(double) * std::max<int64_t>(N, 1));
   p.off_deg = o;        o += align256(sizeof(uint32_t) * (N + 1) + sizeof(int32_t) * (N + 1));
   p.off_scratch = o;    o += 256;
   p.bytes = o;
@@ -335,6 +445,7 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   uint32_t* cell_fill = (uint32_t*)(ws + p.off_cell_fill);
   int32_t* cell_start = (int32_t*)(ws + p.off_cell_start);
   int32_t* cell_atoms = (int32_t*)(ws + p.off_cell_atoms);
+  double* cell_pos = (double*)(ws + p.off_cell_pos);
   int32_t* cell_of = (int32_t*)(ws + p.off_cell_of);
   uint32_t* deg = (uint32_t*)(ws + p.off_deg);
   int32_t* rp_tmp = (int32_t*)(ws + p.off_deg + sizeof(uint32_t) * (n + 1));
@@ -353,8 +464,8 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   k_scan_excl<<<1, 1024, 0, s>>>(cell_count, nc, cell_start, nullptr);
   Grid gr{p.nc[0], p.nc[1], p.nc[2], box[0], box[1], box[2], cutoff * cutoff};
   if (n > 0) {
-    k_cell_place<<<blocks_for(n, 256), 256, 0, s>>>(n, cell_of, cell_start, cell_fill, cell_atoms);
-    k_nb_count<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, deg,
+    k_cell_place<<<blocks_for(n, 256), 256, 0, s>>>(n, pos, cell_of, cell_start, cell_fill, cell_atoms, cell_pos);
+    k_nb_count<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, deg,
                                                  flags);
   }
   k_scan_excl<<<1, 1024, 0, s>>>(deg, n, rp_tmp, total);
@@ -378,7 +489,7 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
 
   k_copy_i32<<<blocks_for(n + 1, 256), 256, 0, s>>>(rp_tmp, row_ptr, n + 1);
   if (n > 0 && host.total > 0) {
-    k_nb_fill<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, row_ptr,
+    k_nb_fill<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, row_ptr,
                                                 rev /* keys staged here */);
     k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, rev, col, shift);
     k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev, flags);
