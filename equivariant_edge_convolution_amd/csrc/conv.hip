@@ -419,13 +419,15 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
     for (int u = 0; u < U; ++u) er[u] = e0 + 64 * u < b ? min(max(rev[e0 + 64 * u], 0), (int)E - 1) : 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = e0 + 64 * u;
-      const bool ok = e < b;
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        ge[u][q] = ok ? g[3 * e + q] : 0.f;
-        gr[u][q] = ok ? g[3 * er[u] + q] : 0.f;
-      }
+      const int e = min(e0 + 64 * u, b - 1);  // rows of 16 bytes: one load per edge
+      const float4 x = *reinterpret_cast<const float4*>(g + 4 * (size_t)e);
+      const float4 y = *reinterpret_cast<const float4*>(g + 4 * (size_t)er[u]);
+      ge[u][0] = x.x;
+      ge[u][1] = x.y;
+      ge[u][2] = x.z;
+      gr[u][0] = y.x;
+      gr[u][1] = y.y;
+      gr[u][2] = y.z;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -559,7 +561,7 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   p.off_A = o;     o += align256(4 * (size_t)p.S * N * NLM * p.C);  // S partial slabs
   p.off_R = o;     o += align256(4 * (size_t)p.chunk * p.NC);
   p.off_Y = o;     o += align256(4 * (size_t)p.chunk * NLM);
-  p.off_g = o;     o += align256(4 * 3 * (size_t)E);
+  p.off_g = o;     o += align256(4 * 4 * (size_t)E);  // dE/dd per edge, padded to 16 bytes
   p.off_ei = o;    o += align256(4 * (size_t)N);
   p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
   p.off_w3t = o;   o += align256(4 * (size_t)p.P * 64 * p.NC);

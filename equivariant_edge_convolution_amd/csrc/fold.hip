@@ -444,9 +444,9 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
   rbar += __shfl_xor(rbar, 32);
   const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
   if (valid && h == 0) {
-    gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
-    gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
-    gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+    *reinterpret_cast<float4*>(gout + 4 * e) =
+        make_float4(rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
+                    rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r, 0.f);
   }
   wave_sync_lds();
 }
@@ -957,9 +957,9 @@ __device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, c
   rbar += __shfl_xor(rbar, 32);
   const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
   if (valid && h == 0) {
-    gout[3 * e + 0] = rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r;
-    gout[3 * e + 1] = rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r;
-    gout[3 * e + 2] = rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r;
+    *reinterpret_cast<float4*>(gout + 4 * e) =
+        make_float4(rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
+                    rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r, 0.f);
   }
   wave_sync_lds();
 }
