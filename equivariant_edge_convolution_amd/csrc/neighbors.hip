@@ -157,6 +157,7 @@ __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const doub
   // The first 64 members of three cells at a time, every load issued before
   // the tests; d = (x_j - x_i) + n L in binary64 as edge_vector forms it.
   constexpr int G = 3;
+#pragma unroll
   for (int o0 = 0; o0 < 27; o0 += G) {
     int c2[G], s[G], sh[G][3], a[G], b[G], j[G];
     double xj[G][3];
