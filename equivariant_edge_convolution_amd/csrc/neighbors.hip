@@ -281,7 +281,41 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
     shift[3 * (a + r) + 1] = (int8_t)((s / 3) % 3 - 1);
     shift[3 * (a + r) + 2] = (int8_t)(s % 3 - 1);
   };
-  if (deg <= SORT_LDS) {
+  if (deg <= 256) {
+    // bitonic sort of up to 256 keys in registers, key x = 4 lane + r: pairs
+    // 4 or more apart across lanes (shuffles), closer pairs within a lane
+    int32_t v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = 4 * lane + r < deg ? keys[a + 4 * lane + r] : INT32_MAX;
+    for (int k = 2; k <= 256; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        if (jj >= 4) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int x = 4 * lane + r;
+            const int32_t o = __shfl_xor(v[r], jj >> 2);
+            const bool lower = (x & jj) == 0, up = (x & k) == 0;
+            v[r] = (lower == up) ? min(v[r], o) : max(v[r], o);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if ((r & jj) != 0) continue;
+            const int r2 = r | jj;
+            const bool up = ((4 * lane + r) & k) == 0;
+            if ((v[r] > v[r2]) == up) {
+              const int32_t t = v[r];
+              v[r] = v[r2];
+              v[r2] = t;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lane + r < deg) emit(4 * lane + r, v[r]);
+  } else if (deg <= SORT_LDS) {
     // bitonic sort of the keys padded to a power of two (the pads sort last)
     int np2 = 64;
     while (np2 < deg) np2 <<= 1;

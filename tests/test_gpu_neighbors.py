@@ -26,6 +26,25 @@ def test_csr_bit_exact(name):
     assert np.array_equal(np_(g.rev), ref.rev)
 
 
+@pytest.mark.parametrize("n_atoms", [150, 600])
+def test_csr_bit_exact_dense_rows(n_atoms):
+    # random atoms in a 6.1 A box with rc = 6.0: rows of about 600 (sorted in
+    # LDS) and 2,400 keys (past the LDS sort: the rank sort), every image kept
+    say(f"[neighbors] dense rows, {n_atoms} atoms")
+    box = np.full(3, 6.1)
+    cfg = I.make_cluster(np.random.default_rng(n_atoms).uniform(0.0, 6.1, (n_atoms, 3)), box)
+    pos = torch.as_tensor(cfg.pos).to(DEV)
+    g = B.build_neighbors(pos, box, 6.0)
+    ref = N.neighbors_celllist(cfg.pos, box, 6.0)
+    deg = np.diff(ref.row_ptr)
+    assert deg.max() > (2048 if n_atoms == 600 else 256)
+    assert g.n_edges == ref.n_edges
+    assert np.array_equal(np_(g.row_ptr), ref.row_ptr)
+    assert np.array_equal(np_(g.col), ref.col)
+    assert np.array_equal(np_(g.shift), ref.shift)
+    assert np.array_equal(np_(g.rev), ref.rev)
+
+
 def test_repeat_is_identical():
     cfg = I.make_config("PV3")
     pos, species, _ = device_inputs(cfg)
