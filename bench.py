@@ -236,7 +236,8 @@ def md_loop(B, torch, cfg, model, dev, steps: int, skin: float, scheme: str, var
     g0 = B.build_neighbors(x0, cfg.box, lc, species, S)
     cap = int(1.25 * g0.n_edges) + 1024
     lists = [B.NeighborList(n, cfg.box, lc, cap, dev, species, S) for _ in range(2)]
-    ef = B.EnergyForces(g0, model, dev, atom_energy=False, variant=variant, edge_capacity=cap)
+    table = B.RadialTable(model, 6) if variant == "tabulated" else None
+    ef = B.EnergyForces(g0, model, dev, atom_energy=False, variant=variant, edge_capacity=cap, table=table)
     main = torch.cuda.current_stream(dev)
     side = torch.cuda.Stream(device=dev) if scheme == "side" else None
     total = warmup + steps
