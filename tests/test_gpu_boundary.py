@@ -26,15 +26,27 @@ def _same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("variant", ["direct", "folded"])
+def _ef(g, pos, box, species, model, variant, **kw):
+    """energy_forces of a variant; the tabulated one with a table built here."""
+    table = B.RadialTable(model, 5) if variant == "tabulated" else None
+    return B.energy_forces(g, pos, box, species, model, variant=variant, table=table, **kw), table
+
+
+VARIANTS = ["direct", "folded", "tabulated"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_inputs_are_never_written(variant):
     say(f"[boundary] inputs untouched {variant}")
     cfg = I.make_config("PV3")
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
+    table = B.RadialTable(model, 5) if variant == "tabulated" else None
     ins = [pos, species, g.row_ptr, g.col, g.shift, g.rev, model.W1, model.W2, model.W3, model.emb, model.w_read]
+    if table is not None:
+        ins += [table.coef, table.level]
     before = _snapshot(ins)
-    B.energy_forces(g, pos, cfg.box, species, model, virial=True, variant=variant)
+    B.energy_forces(g, pos, cfg.box, species, model, virial=True, variant=variant, table=table)
     B.edge_message(g, pos, cfg.box, species, model)
     _, basis, _ = B.radial_basis(g, pos, cfg.box, cfg.model.cutoff)
     b_before = _snapshot([basis])
@@ -71,7 +83,7 @@ def test_overlapping_output_is_rejected():
     assert B.STATUS[st] == "EEC_ERR_ALIAS"
 
 
-@pytest.mark.parametrize("variant", ["direct", "folded"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_empty_and_edgeless_cells(variant):
     model = B.Model.from_arrays(I.draw_model(1, 64), DEV)
     box = np.full(3, 30.0)
@@ -79,20 +91,20 @@ def test_empty_and_edgeless_cells(variant):
     pos = torch.zeros((0, 3), dtype=torch.float64, device=DEV)
     sp = torch.zeros(0, dtype=torch.int32, device=DEV)
     g = B.build_neighbors(pos, box, 6.0)
-    out = B.energy_forces(g, pos, box, sp, model, variant=variant)
+    out, _ = _ef(g, pos, box, sp, model, variant)
     assert float(out["energy"].cpu()[0]) == 0.0
     # atoms, no edges
     pos = torch.tensor([[1.0, 1.0, 1.0], [15.0, 15.0, 15.0], [25.0, 3.0, 9.0]], dtype=torch.float64, device=DEV)
     sp = torch.zeros(3, dtype=torch.int32, device=DEV)
     g = B.build_neighbors(pos, box, 6.0)
     assert g.n_edges == 0
-    out = B.energy_forces(g, pos, box, sp, model, virial=True, variant=variant)
+    out, _ = _ef(g, pos, box, sp, model, variant, virial=True)
     assert float(out["energy"].cpu()[0]) == 0.0
     assert np.all(np_(out["forces"]) == 0.0) and np.all(np_(out["atom_energy"]) == 0.0)
     assert np.all(np_(out["virial"]) == 0.0)
 
 
-@pytest.mark.parametrize("variant", ["direct", "folded"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_isolated_atom_among_others(variant):
     # a trimer plus one far atom: the lone atom has zero energy and force
     box = np.full(3, 40.0)
@@ -101,7 +113,7 @@ def test_isolated_atom_among_others(variant):
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
     assert g.n_edges == 6
-    out = B.energy_forces(g, pos, cfg.box, species, model, variant=variant)
+    out, _ = _ef(g, pos, cfg.box, species, model, variant)
     ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
     F = np_(out["forces"])
     assert np.all(F[3] == 0.0) and float(np_(out["atom_energy"])[3]) == 0.0
