@@ -24,12 +24,6 @@ namespace {
 
 constexpr int SORT_LDS = 2048;  // keys a row-sort wave stages in LDS
 
-__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
-  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
-       k += (int64_t)gridDim.x * blockDim.x)
-    p[k] = v;
-}
-
 // counters[c] += 1 for every active lane, one atomic per distinct c in the
 // wave; returns the lane's slot (the counter's old value plus its rank among
 // the lanes with the same c).  Slots within a cell depend on the order the
@@ -50,6 +44,17 @@ __device__ __forceinline__ uint32_t wave_count(uint32_t* __restrict__ counters, 
     pending &= ~same;
   }
   return slot;
+}
+
+// Clears the cell counts and fills and the 16-byte flags / edge-total word.
+__global__ void k_nb_clear(uint32_t* __restrict__ cell_count, uint32_t* __restrict__ cell_fill, int64_t nc,
+                           uint32_t* __restrict__ flags) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < 4) flags[t] = 0u;
+  for (int64_t k = t; k < nc; k += (int64_t)gridDim.x * blockDim.x) {
+    cell_count[k] = 0u;
+    cell_fill[k] = 0u;
+  }
 }
 
 __global__ void k_nb_bin(int32_t n, const double* __restrict__ pos, double Lx, double Ly, double Lz,
@@ -488,9 +493,8 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   int64_t* total = (int64_t*)(ws + p.off_scratch + 8);
 
   const int64_t nc = p.n_cells;
-  k_fill_u32<<<blocks_for(2 * nc, 256), 256, 0, s>>>(cell_count, nc, 0u);
-  k_fill_u32<<<blocks_for(nc, 256), 256, 0, s>>>(cell_fill, nc, 0u);
-  k_fill_u32<<<1, 64, 0, s>>>(flags, 4, 0u);
+  k_nb_clear<<<(int)std::max<int64_t>(1, std::min<int64_t>(blocks_for(nc, 256), 1024)), 256, 0, s>>>(
+      cell_count, cell_fill, nc, flags);
   if (n > 0) {
     k_nb_bin<<<blocks_for(n, 256), 256, 0, s>>>(n, pos, box[0], box[1], box[2], p.nc[0], p.nc[1],
                                                  p.nc[2], species, n_species, cell_of, cell_count,
@@ -504,17 +508,28 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
                                                  flags);
   }
   k_scan_excl<<<1, 1024, 0, s>>>(deg, n, rp_tmp, total);
-  struct {
+  // The flags and the edge total come back through a 16-byte pinned host word
+  // kept per host thread (a copy into pageable memory is staged, and cost as
+  // much as the kernels on small cells); allocated on the first build.
+  struct Readback {
     uint32_t flags;
     uint32_t pad;
     int64_t total;
-  } host{};
-  if (hipMemcpyAsync(&host.flags, flags, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipMemcpyAsync(&host.total, total, 8, hipMemcpyDeviceToHost, s) != hipSuccess ||
+  };
+  static_assert(sizeof(Readback) == 16, "flags word, pad and edge total");
+  thread_local Readback* pinned = nullptr;
+  if (pinned == nullptr &&
+      hipHostMalloc((void**)&pinned, sizeof(Readback), hipHostMallocPortable) != hipSuccess) {
+    pinned = nullptr;
+    *why = "HIP error while allocating the edge-count readback word";
+    return EEC_ERR_HIP;
+  }
+  if (hipMemcpyAsync(pinned, flags, sizeof(Readback), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {
     *why = "HIP error while reading the edge count";
     return EEC_ERR_HIP;
   }
+  const Readback host = *pinned;
   if (host.flags & FLAG_OUT_OF_BOX) { *why = "a position is non-finite or outside [0, L)"; return EEC_ERR_OUT_OF_BOX; }
   if (host.flags & FLAG_SPECIES) { *why = "a species index is outside [0, n_species)"; return EEC_ERR_SPECIES; }
   if (host.flags & FLAG_GEOMETRY) { *why = "two atoms (or periodic images) coincide"; return EEC_ERR_GEOMETRY; }

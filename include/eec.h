@@ -23,7 +23,8 @@
  * Conventions (all entry points)
  *   - Arrays are row-major and contiguous.  Pointers are DEVICE pointers unless
  *     marked [host].
- *   - The caller owns every buffer.  The library never allocates device memory,
+ *   - The caller owns every buffer.  The library never allocates device memory
+ *     (eec_build_neighbors keeps one 16-byte pinned host word per thread),
  *     never writes an input, and rejects output ranges that overlap an input or
  *     another output (EEC_ERR_ALIAS).  Scratch comes from the caller's
  *     `workspace` (device, 256-byte aligned), sized by the *_workspace_bytes
@@ -132,9 +133,10 @@ typedef struct {
  *              EEC_ERR_CAPACITY (then it is the capacity required and the CSR
  *              arrays are not written).
  *   workspace  >= eec_neighbors_workspace_bytes(n_atoms, box, cutoff) bytes
- * Synchronises `stream` once (to read E and the validity flags); the CSR
- * arrays are written after that, on `stream`, so work on another stream that
- * reads them must wait for `stream` (an event).  The out-of-box, species and
+ * Synchronises `stream` once (to read E and the validity flags, through a
+ * 16-byte pinned host word that the library allocates on a thread's first
+ * call and keeps); the CSR arrays are written after that, on `stream`, so
+ * work on another stream that reads them must wait for `stream` (an event).  The out-of-box, species and
  * coincident-atom checks are made on the device before any CSR array is
  * written.  A list built with a cutoff larger than the model's (a Verlet skin)
  * serves the compute entry points unchanged: see eec_skin_check. */
