@@ -95,6 +95,9 @@ WORKLOADS = {
 }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
 def sources_digest() -> str:
     """SHA-256 over the kernel sources (csrc/*.hip, csrc/*.hpp, by name)."""
     import hashlib
@@ -114,7 +117,7 @@ def recorded_traffic(kernel: str, config_name: str):
     calibration there; None unless the record is for this workload and the
     kernel sources are still the ones that were counted."""
     try:
-        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+        with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
