@@ -29,7 +29,8 @@ def _run(name, virial=False, variant="direct"):
     cfg = I.make_config(name)
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
-    out = B.energy_forces(g, pos, cfg.box, species, model, virial=virial, variant=variant)
+    table = B.RadialTable(model, 6) if variant == "tabulated" else None
+    out = B.energy_forces(g, pos, cfg.box, species, model, virial=virial, variant=variant, table=table)
     return cfg, pos, species, model, g, {k: np_(v) for k, v in out.items()}
 
 
@@ -132,7 +133,7 @@ def test_edge_message_full_size_sampled(name):
         assert np.abs(A[i] - A0).max() <= 2e-5 * np.abs(A0).max(), i
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + ["tabulated"])
 @pytest.mark.parametrize("name,n_e,n_f", [("D4096", 256, 3), ("RS", 256, 6), ("PV", 256, 4), ("D32k", 96, 2)])
 def test_full_size_sampled(name, n_e, n_f, variant):
     """Full-size cells in the benchmark's launch configuration; exact per-atom
@@ -189,8 +190,9 @@ def test_timed_entry_point_matches_untimed():
     cfg = I.make_config("RS3")
     pos, species, model = device_inputs(cfg)
     g = graph_for(cfg, pos, species)
-    for variant in VARIANTS:
-        ef = B.EnergyForces(g, model, pos.device, variant=variant)
+    for variant in VARIANTS + ["tabulated"]:
+        table = B.RadialTable(model, 5) if variant == "tabulated" else None
+        ef = B.EnergyForces(g, model, pos.device, variant=variant, table=table)
         ef(pos, cfg.box, species)
         E, F = ef.energy.clone(), ef.forces.clone()
         ev = B.HipEvents(2 * len(B.PHASES))
