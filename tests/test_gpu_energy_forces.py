@@ -201,3 +201,24 @@ def test_timed_entry_point_matches_untimed():
         assert torch.equal(ef.energy, E) and torch.equal(ef.forces, F)
         assert all(ev.elapsed_ms(2 * k, 2 * k + 1) >= 0 for k in range(len(B.PHASES)))
         ev.close()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name,channels", [("D64", 64), ("D512", 64), ("D64", 128)])
+def test_four_species(name, channels, variant):
+    """The largest species count: the diamond cell with species 0-3 in turn
+    and a four-species model (16 ordered pairs; the folded call takes the
+    separate forward / readout / backward kernels)."""
+    say(f"[four species] {name} C={channels} {variant}")
+    base = I.make_config(name)
+    cfg = I.make_cluster(base.pos, base.box, species=np.arange(base.n_atoms) % 4, n_species=4,
+                         channels=channels, seed=4)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    got = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, virial=True,
+                                                   variant=variant).items()}
+    ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+    assert np.abs(got["virial"] - ref["virial"]).max() <= 1e-4 * np.abs(ref["virial"]).max()
