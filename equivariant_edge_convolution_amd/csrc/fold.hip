@@ -530,6 +530,46 @@ __device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane
   return 0.5f * esum;
 }
 
+// The readout of one receiver by the W = 8 waves of a workgroup: T (the sum of
+// the waves' partials, in wave order) into tw, then wave w forms M for
+// harmonics 2w and 2w + 1 (lane = hidden unit k, G_l read from global memory
+// along rows: G is symmetric) into msh, and its share of E_i = 1/2 sum T.M
+// into esh[w].  Returns E_i (the shares in wave order) to every thread.
+template <int W, int TSM_OFF, int STRIDE>
+__device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wbase, const float* __restrict__ G,
+                                                     int lane, int wave, float (*msh)[HID + 1], float* esh) {
+  static_assert(W == 8, "two harmonics per wave");
+  for (int e = threadIdx.x; e < HID * NLM; e += 64 * W) {
+    float v = tw[e];
+#pragma unroll
+    for (int w = 1; w < W; ++w) v += wbase[w * STRIDE + TSM_OFF + e];
+    tw[e] = v;
+  }
+  __syncthreads();
+  const float(*tsm)[NLM] = reinterpret_cast<const float(*)[NLM]>(tw);
+  const int lm0 = 2 * wave, lm1 = lm0 + 1;
+  const int l0 = lm0 == 0 ? 0 : (lm0 < 4 ? 1 : (lm0 < 9 ? 2 : 3));
+  const int l1 = lm1 < 4 ? 1 : (lm1 < 9 ? 2 : 3);
+  const float* g0 = G + (size_t)l0 * HID * HID + lane;
+  const float* g1 = G + (size_t)l1 * HID * HID + lane;
+  float m0 = 0.f, m1 = 0.f;
+#pragma unroll 8
+  for (int kk = 0; kk < HID; ++kk) {
+    m0 += g0[kk * HID] * tsm[kk][lm0];
+    m1 += g1[kk * HID] * tsm[kk][lm1];
+  }
+  msh[lm0][lane] = m0;
+  msh[lm1][lane] = m1;
+  float es = tsm[lane][lm0] * m0 + tsm[lane][lm1] * m1;
+  for (int off = 32; off > 0; off >>= 1) es += __shfl_xor(es, off);
+  if (lane == 0) esh[wave] = es;
+  __syncthreads();
+  float e = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) e += esh[w];
+  return 0.5f * e;
+}
+
 // ------------------------------------------------------------------ fused (one species)
 // With one species, receiver i's unit holds its whole row, and the backward of
 // the unit needs only M_i, which depends on nothing but the unit's own forward:
@@ -655,6 +695,7 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   __shared__ float w12[W12_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   __shared__ __align__(16) float msh[NLM][HID + 1];  // M of the receiver, read by every wave
+  __shared__ float esh[W];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
   const float* w1s = w12;
@@ -680,23 +721,10 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
 #pragma unroll
       for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
     __syncthreads();
-    if (wave == 0) {
-      // T = sum of the waves' partials, in wave order (lane: 16 consecutive entries)
-      float* tw = &L.tsm[0][0];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = tw[16 * lane + e];
-#pragma unroll
-        for (int w = 1; w < W; ++w) v += wbuf[w][FoldLds<C>::TSM + 16 * lane + e];
-        tw[16 * lane + e] = v;
-      }
-      wave_sync_lds();
-      float macc[NLM];
-      const float* gl = G + lane;
-      const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return gl[(l * HID + kk) * HID]; }, macc);
-      if (lane == 0) ei[i] = e2;
-#pragma unroll
-      for (int lm = 0; lm < NLM; ++lm) msh[lm][lane] = macc[lm];
+    {
+      const float e2 = gram_epilogue_split<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(
+          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh, esh);
+      if (threadIdx.x == 0) ei[i] = e2;
     }
     __syncthreads();
     j = 0;
@@ -972,6 +1000,7 @@ k_fold_split_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G,
                    float* __restrict__ gout, float* __restrict__ stash) {
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   __shared__ __align__(16) float msh[NLM][HID + 1];  // M of the receiver, read by every wave
+  __shared__ float esh[W];
   __shared__ float4 tpb[W][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
@@ -994,23 +1023,10 @@ k_fold_split_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G,
 #pragma unroll
       for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
     __syncthreads();
-    if (wave == 0) {
-      // T = sum of the waves' partials, in wave order (lane: 16 consecutive entries)
-      float* tw = &L.tsm[0][0];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = tw[16 * lane + e];
-#pragma unroll
-        for (int w = 1; w < W; ++w) v += wbuf[w][FoldLds<C>::TSM + 16 * lane + e];
-        tw[16 * lane + e] = v;
-      }
-      wave_sync_lds();
-      float macc[NLM];
-      const float* gl = G + lane;
-      const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return gl[(l * HID + kk) * HID]; }, macc);
-      if (lane == 0) ei[i] = e2;
-#pragma unroll
-      for (int lm = 0; lm < NLM; ++lm) msh[lm][lane] = macc[lm];
+    {
+      const float e2 = gram_epilogue_split<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(
+          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh, esh);
+      if (threadIdx.x == 0) ei[i] = e2;
     }
     __syncthreads();
     j = 0;
