@@ -30,6 +30,8 @@ struct Lds {
 struct EdgeIn {
   const double* pos;
   double Lx, Ly, Lz, rc;
+  double inv_rc;              // 1 / rc
+  float inv_rc_f;             // 1 / rc rounded to float32
   const int32_t* recv;
   const int32_t* col;
   const int8_t* shift;

@@ -175,6 +175,96 @@ __device__ __forceinline__ void basis16(double r, double rc, int n0, float b[16]
   basis16_from<DERIV>(st, r, rc, n0, b, db);
 }
 
+// Float32 basis of the folded kernels (float32, as the rest of the network).
+// x = r / rc is carried as a float32 head and tail.  Lane half h starts its
+// recurrence from the angle pi x (h = 0) or 16 pi x (h = 1; 16 x is exact in
+// float32): sincospif of the head, corrected to first order by the tail, so
+// both starts carry the binary64 x and neither is built by angle doublings
+// (whose errors grow with every doubling and bias the upper half).
+struct BasisSeed {
+  float x, xl;    // r / rc: float32 head and tail
+  float s1, c1;   // sin, cos of pi x (every lane)
+  float sa, ca;   // sin, cos of m pi x, m = 1 (h = 0) or 16 (h = 1)
+  float inv_r;
+};
+
+// Lanes 0-31 of v to both halves of the wave.
+__device__ __forceinline__ float lower_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ void sincos_pi_split(float xh, float xl, float m, float& s, float& c) {
+  float sh, ch;
+  sincospif(m * xh, &sh, &ch);
+  const float d = (float)PI * (m * xl);
+  s = fmaf(d, ch, sh);
+  c = fmaf(-d, sh, ch);
+}
+
+// The seed of an edge from its binary64 length (lane half h; the two halves of
+// the wave hold the same edges).
+__device__ __forceinline__ BasisSeed basis_seed(double r, double inv_rc, float inv_r, int h) {
+  const double xd = r * inv_rc;
+  BasisSeed sd;
+  sd.x = (float)xd;
+  sd.xl = (float)(xd - (double)sd.x);
+  sincos_pi_split(sd.x, sd.xl, h ? 16.f : 1.f, sd.sa, sd.ca);
+  sd.s1 = lower_half(sd.sa);
+  sd.c1 = lower_half(sd.ca);
+  sd.inv_r = inv_r;
+  return sd;
+}
+
+// The same seed from a stored head, tail, sin pi x and cos pi x.
+__device__ __forceinline__ BasisSeed basis_seed_stored(float x, float xl, float s1, float c1, float inv_r, int h) {
+  BasisSeed sd;
+  sd.x = x;
+  sd.xl = xl;
+  sd.s1 = s1;
+  sd.c1 = c1;
+  sincos_pi_split(x, xl, h ? 16.f : 1.f, sd.sa, sd.ca);
+  sd.inv_r = inv_r;
+  return sd;
+}
+
+// Basis functions n = 16 h + 1 .. 16 h + 16 of a lane half h in float32 (and
+// db_n / dr) by the three-term recurrence sin((n+1)t) = 2 cos t sin(nt) -
+// sin((n-1)t) (and the same for cos); half 1 starts at n = 17 by one rotation
+// of its 16 pi x by pi x.  The envelope is zero from x = 1 on, so past the
+// cutoff every b_n and db_n is an exact zero.
+template <bool DERIV>
+__device__ __forceinline__ void basis16f(const BasisSeed& sd, float inv_rc, int h, float b[16], float db[16]) {
+  const float s17 = fmaf(sd.sa, sd.c1, sd.ca * sd.s1), c17 = fmaf(sd.ca, sd.c1, -(sd.sa * sd.s1));
+  float sn = h ? s17 : sd.s1, cn = h ? c17 : sd.c1;
+  float sp = h ? sd.sa : 0.f, cp = h ? sd.ca : 1.f;
+  const float x = sd.x;
+  float env = 0.f, envd = 0.f;
+  if (x < 1.f) {
+    const float x2 = x * x, x5 = x2 * x2 * x, x6 = x5 * x, om = 1.f - x;
+    env = fmaf(x6, fmaf(x, fmaf(-21.f, x, 48.f), -28.f), 1.f);
+    envd = -168.f * x5 * om * om * inv_rc;
+  }
+  const float A = sd.inv_r * env;                            // b_n = s_n A
+  const float Bd = DERIV ? sd.inv_r * (envd - A) : 0.f;     // db_n = c_n n (pi / rc) A + s_n Bd
+  const float kA0 = (float)PI * inv_rc * A;
+  const float two_c1 = 2.f * sd.c1;
+  const int n0 = 16 * h + 1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    b[k] = sn * A;
+    if (DERIV) {
+      db[k] = fmaf(cn, (float)(n0 + k) * kA0, sn * Bd);
+      const float cx = fmaf(two_c1, cn, -cp);
+      cp = cn;
+      cn = cx;
+    }
+    const float sx = fmaf(two_c1, sn, -sp);
+    sp = sn;
+    sn = sx;
+  }
+}
+
 // ---------------------------------------------------------------- harmonics
 // Real component-normalised harmonics l <= 3 of a unit vector (x, y, z),
 // flat index l*l + l + m, m = -l..l, z polar, no Condon-Shortley phase.

@@ -58,7 +58,8 @@ struct WaveLds {
 // radial basis and the first two layers.  Row of an edge (ZROW floats):
 //   [0, 64)    silu'(z1) by hidden index
 //   [64, 128)  z2 by hidden index
-//   [128, 136) u_x, u_y, u_z, 1/r (float32), r (binary64 as two words), 2 spare
+//   [128, 136) u_x, u_y, u_z, 1/r, and the basis seed: x = r / rc as a float32
+//              head and tail, sin pi x, cos pi x
 // A unit's first STASH_TILES tiles are kept; further tiles (rows denser than
 // STASH_TILES * 32 edges) recompute.  The live rows of all waves (about 85 MB
 // for a 4096-atom diamond) stay in the last-level cache between the forward
@@ -101,17 +102,16 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
                                          int q0, int qa, int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
+  const BasisSeed sd = basis_seed(g.r, in.inv_rc, g.inv_r, h);
   if (zs != nullptr && valid && h == 0) {
     float* row = zs + s * ZROW + 2 * HID;
-    float rw[2];
-    __builtin_memcpy(rw, &g.r, sizeof(double));
     *reinterpret_cast<float4*>(row) = make_float4(g.ux, g.uy, g.uz, g.inv_r);
-    *reinterpret_cast<float2*>(row + 4) = make_float2(rw[0], rw[1]);
+    *reinterpret_cast<float4*>(row + 4) = make_float4(sd.x, sd.xl, sd.s1, sd.c1);
   }
   f32x16 z[2], a[2];
   {
     float bas[16];
-    basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+    basis16f<false>(sd, in.inv_rc_f, h, bas, nullptr);
     layer1(w1s, bas, s, h, z);
   }
   if (zs != nullptr) {
@@ -317,16 +317,17 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
   const bool valid = q0 + s < qb;
   const int64_t e = tile_edge(perm, q0, qa, qb, s);
   Geo g;
+  BasisSeed sd;
   f32x16 d1[2], d2[2], s2[2];  // silu'(z1), silu'(z2), silu(z2); edges on N
   if (zs != nullptr) {
     const float* row = zs + (valid ? s : 0) * ZROW;
     const float4 u = *reinterpret_cast<const float4*>(row + 2 * HID);
-    const float2 rw = *reinterpret_cast<const float2*>(row + 2 * HID + 4);
+    const float4 bs = *reinterpret_cast<const float4*>(row + 2 * HID + 4);
     g.ux = u.x;
     g.uy = u.y;
     g.uz = u.z;
     g.inv_r = u.w;
-    __builtin_memcpy(&g.r, &rw, sizeof(double));
+    sd = basis_seed_stored(bs.x, bs.y, bs.z, bs.w, u.w, h);
     f32x16 z[2], s1[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -340,10 +341,11 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
     silu_and_deriv(z, s2, d2);
   } else {
     g = geo_from_raw(in, edge_raw(in, e), xi.x);
+    sd = basis_seed(g.r, in.inv_rc, g.inv_r, h);
     f32x16 z[2], s1[2];
     {
       float bas[16];
-      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+      basis16f<false>(sd, in.inv_rc_f, h, bas, nullptr);
       layer1(w1s, bas, s, h, z);
     }
     silu_and_deriv(z, s1, d1);
@@ -437,7 +439,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
   float rbar = 0.f;
   {
     float bas[16], dbas[16];
-    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);  // cheaper to redo than to keep live
+    basis16f<true>(sd, in.inv_rc_f, h, bas, dbas);  // cheaper to redo than to keep live
 #pragma unroll
     for (int r = 0; r < 16; ++r) rbar += bb[r] * dbas[r];
   }
@@ -1252,6 +1254,8 @@ EdgeIn make_in_f(const ConvPlan& p, const eec_graph* g, const double* pos, Box b
   in.Ly = box.L[1];
   in.Lz = box.L[2];
   in.rc = cutoff;
+  in.inv_rc = 1.0 / cutoff;
+  in.inv_rc_f = (float)(1.0 / cutoff);
   in.recv = nullptr;  // the unit kernels know each edge's receiver
   in.col = g->col;
   in.shift = g->shift;

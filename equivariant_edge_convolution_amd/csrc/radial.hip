@@ -416,6 +416,8 @@ EdgeIn make_in(const ConvPlan& p, const eec_graph* g, const double* pos, Box box
   in.Ly = box.L[1];
   in.Lz = box.L[2];
   in.rc = cutoff;
+  in.inv_rc = 1.0 / cutoff;
+  in.inv_rc_f = (float)(1.0 / cutoff);
   in.recv = (const int32_t*)(ws + p.off_recv);
   in.col = g->col;
   in.shift = g->shift;
