@@ -93,7 +93,8 @@ __device__ double block_max(double v, double* red) {
 // the binary64 interpolants checked against the network at CHECKS points per
 // sub-piece; the first level whose errors (values and r-derivatives, relative
 // to each unit's largest magnitude over the sub-piece) are all <= TAB_TOL is
-// kept (else the last).  Slots f < 2^d of c hold its sub-pieces.
+// kept (else the last).  Slots f < 2^d of c hold its sub-pieces, the unused
+// slots f >= 2^d zeros (every word of the table is written).
 __global__ void __launch_bounds__(TAB_T) k_table_build(int K, double rc, const float* __restrict__ W1,
                                                        const float* __restrict__ W2, float* __restrict__ tab,
                                                        int32_t* __restrict__ level,
@@ -105,6 +106,7 @@ __global__ void __launch_bounds__(TAB_T) k_table_build(int K, double rc, const f
   const float* w2 = W2 + (size_t)p * HID * HID;
   const double h0 = rc / (double)nc;
   double cv = 0.0, cd = 0.0;  // certificate of the kept level (float32 coefficients)
+  int kept = TAB_DMAX;
   for (int d = 0; d <= TAB_DMAX; ++d) {
     const int nf = 1 << d;
     const double h = ldexp(h0, -d);
@@ -187,8 +189,13 @@ __global__ void __launch_bounds__(TAB_T) k_table_build(int K, double rc, const f
     const double worst = block_max(fmax(tv, td), red);
     if (worst <= TAB_TOL || d == TAB_DMAX) {
       if (j == 0) level[p * nc + c] = d;
+      kept = d;
       break;
     }
+  }
+  for (int f = 1 << kept; f < TAB_SUB; ++f) {
+    float* out = tab + (((size_t)(p * nc + c) * TAB_SUB + f) * TAB_NC) * HID + 2 * (j & 31) + (j >> 5);
+    for (int m = 0; m < TAB_NC; ++m) out[m * HID] = 0.f;
   }
   if (cert != nullptr) {
     atomicMax(cert, (unsigned long long)__double_as_longlong(cv));

@@ -280,7 +280,8 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
  * first kind, the interpolant stored in float32 in power form in the
  * sub-piece variable t in [-1, 1], r = c h0 + (f + (t + 1) / 2) h0 / 2^d(c):
  *   coef[p][c][f][m][j % 32][j / 32] = a_m of unit j,  s2_j(r) ~ sum_m a_m t^m
- *   (16 sub-piece slots per coarse piece, f < 2^d(c) used), level[p][c] = d(c).
+ *   (16 sub-piece slots per coarse piece, f < 2^d(c) used, the others written
+ *   as zeros), level[p][c] = d(c).
  *   m            the model (W1, W2 and the cutoff are read)
  *   log2_pieces  in [2, 10]; 6 is the default of the binding
  *   coef         device float32, coef_floats >= eec_radial_table_floats(m, log2_pieces)
