@@ -466,10 +466,17 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
   }
 }
 
-// Forces of every atom.  The per-atom energies are complete before this
-// kernel starts, so when `energy` is given one extra workgroup (the last) forms
-// their total alongside the scatter and the call needs no reduction launch for
-// it; the virial total needs the whole scatter and runs after it (k_totals).
+// Forces of every atom, one wave per atom.  The per-atom energies are
+// complete before this kernel starts, so when `energy` is given one extra
+// workgroup (the first, so that it runs beside the scatter rather than after
+// it) forms their total and the call needs no reduction launch for it; the
+// virial total needs the whole scatter and runs after it (k_totals).
+// Workgroups go to the eight XCDs in turn (workgroup b to XCD b mod 8), so
+// scatter workgroup v takes atom block (v mod 8) nv / 8 + v / 8 (nv, the
+// number of scatter workgroups, a multiple of 8): each XCD works through one
+// contiguous range of atoms, and the reverse-edge rows that neighbouring
+// atoms gather (adjacent rows of a shared neighbour, one cache line) are
+// fetched into its L2 once instead of once per XCD.
 template <bool VIRIAL>
 __global__ void __launch_bounds__(TT) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
                                                 const int32_t* __restrict__ col,
@@ -479,13 +486,16 @@ __global__ void __launch_bounds__(TT) k_scatter(int32_t n, int64_t E, const int3
                                                 double Lz, const float* __restrict__ g,
                                                 float* __restrict__ F, double* __restrict__ vpart,
                                                 const float* __restrict__ ei, float* __restrict__ energy) {
-  const int nblk = gridDim.x - (energy != nullptr ? 1 : 0);
-  if ((int)blockIdx.x == nblk) {
+  const int first = energy != nullptr ? 1 : 0;
+  const int nblk = gridDim.x - first;
+  if (first && blockIdx.x == 0) {
     block_totals<false>(n, ei, nullptr, energy, nullptr);
     return;
   }
+  const int v = blockIdx.x - first;
+  const int xv = (v & 7) * (nblk >> 3) + (v >> 3);
   const int lane = threadIdx.x & 63;
-  for (int i = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TT) >> 6)
+  for (int i = (int)((xv * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TT) >> 6)
     scatter_atom<VIRIAL>(i, lane, n, E, rp, col, shift, rev, pos, Lx, Ly, Lz, g, F, vpart);
 }
 
@@ -629,7 +639,7 @@ void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
       k_totals<false><<<1, TT, 0, s>>>(0, ei, vpart, energy, virial);
     return;
   }
-  const int grid = blocks_for(p.N, TT / 64);
+  const int grid = (blocks_for(p.N, TT / 64) + 7) & ~7;  // a multiple of 8 (k_scatter's XCD mapping)
   if (virial) {
     k_scatter<true><<<grid, TT, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0], box.L[1],
                                          box.L[2], gin, forces, vpart, ei, nullptr);
