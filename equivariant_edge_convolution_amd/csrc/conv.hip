@@ -350,17 +350,18 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, int nparts, const fl
 }
 
 // ------------------------------------------------------------ totals
-// Totals of one 256-thread workgroup, in binary64 with a fixed order: each
+// Totals of one workgroup of NTH threads, in binary64 with a fixed order: each
 // thread a contiguous slice of atoms, then a tree.  E = sum_i E_i; with VIRIAL,
 // W = sum_i vpart_i.
-constexpr int TT = 256;
-template <bool VIRIAL>
+constexpr int TT = 256;   // k_totals
+constexpr int TS = 1024;  // k_scatter: 16 atoms per workgroup
+template <bool VIRIAL, int NTH>
 __device__ void block_totals(int32_t n, const float* __restrict__ ei, const double* __restrict__ vpart,
                              float* __restrict__ energy, float* __restrict__ virial) {
   constexpr int NT = VIRIAL ? 10 : 1;
-  __shared__ double part[NT][TT];
+  __shared__ double part[NT][NTH];
   const int t = threadIdx.x;
-  const int per = (n + TT - 1) / TT;
+  const int per = (n + NTH - 1) / NTH;
   const int a = std::min(n, t * per), b = std::min(n, a + per);
   double acc[NT];
 #pragma unroll
@@ -374,7 +375,7 @@ __device__ void block_totals(int32_t n, const float* __restrict__ ei, const doub
 #pragma unroll
   for (int k = 0; k < NT; ++k) part[k][t] = acc[k];
   __syncthreads();
-  for (int o = TT / 2; o > 0; o >>= 1) {
+  for (int o = NTH / 2; o > 0; o >>= 1) {
     if (t < o)
 #pragma unroll
       for (int k = 0; k < NT; ++k) part[k][t] += part[k][t + o];
@@ -389,7 +390,7 @@ template <bool VIRIAL>
 __global__ void __launch_bounds__(TT) k_totals(int32_t n, const float* __restrict__ ei,
                                                const double* __restrict__ vpart, float* __restrict__ energy,
                                                float* __restrict__ virial) {
-  block_totals<VIRIAL>(n, ei, vpart, energy, virial);
+  block_totals<VIRIAL, TT>(n, ei, vpart, energy, virial);
 }
 
 // ------------------------------------------------------------ force scatter
@@ -466,7 +467,10 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
   }
 }
 
-// Forces of every atom, one wave per atom.  The per-atom energies are
+// Forces of every atom, one wave per atom, 16 atoms per workgroup (the
+// gathered reverse-edge rows of consecutive atoms are adjacent rows of their
+// shared neighbours: a workgroup's waves reuse each other's cache lines in the
+// CU's L1).  The per-atom energies are
 // complete before this kernel starts, so when `energy` is given one extra
 // workgroup (the first, so that it runs beside the scatter rather than after
 // it) forms their total and the call needs no reduction launch for it; the
@@ -478,7 +482,7 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
 // atoms gather (adjacent rows of a shared neighbour, one cache line) are
 // fetched into its L2 once instead of once per XCD.
 template <bool VIRIAL>
-__global__ void __launch_bounds__(TT) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
+__global__ void __launch_bounds__(TS) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
                                                 const int32_t* __restrict__ col,
                                                 const int8_t* __restrict__ shift,
                                                 const int32_t* __restrict__ rev,
@@ -489,13 +493,13 @@ __global__ void __launch_bounds__(TT) k_scatter(int32_t n, int64_t E, const int3
   const int first = energy != nullptr ? 1 : 0;
   const int nblk = gridDim.x - first;
   if (first && blockIdx.x == 0) {
-    block_totals<false>(n, ei, nullptr, energy, nullptr);
+    block_totals<false, TS>(n, ei, nullptr, energy, nullptr);
     return;
   }
   const int v = blockIdx.x - first;
   const int xv = (v & 7) * (nblk >> 3) + (v >> 3);
   const int lane = threadIdx.x & 63;
-  for (int i = (int)((xv * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TT) >> 6)
+  for (int i = (int)((xv * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TS) >> 6)
     scatter_atom<VIRIAL>(i, lane, n, E, rp, col, shift, rev, pos, Lx, Ly, Lz, g, F, vpart);
 }
 
@@ -639,13 +643,13 @@ void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
       k_totals<false><<<1, TT, 0, s>>>(0, ei, vpart, energy, virial);
     return;
   }
-  const int grid = (blocks_for(p.N, TT / 64) + 7) & ~7;  // a multiple of 8 (k_scatter's XCD mapping)
+  const int grid = (blocks_for(p.N, TS / 64) + 7) & ~7;  // a multiple of 8 (k_scatter's XCD mapping)
   if (virial) {
-    k_scatter<true><<<grid, TT, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0], box.L[1],
+    k_scatter<true><<<grid, TS, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0], box.L[1],
                                          box.L[2], gin, forces, vpart, ei, nullptr);
     k_totals<true><<<1, TT, 0, s>>>(p.N, ei, vpart, energy, virial);
   } else {
-    k_scatter<false><<<grid + 1, TT, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0],
+    k_scatter<false><<<grid + 1, TS, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0],
                                               box.L[1], box.L[2], gin, forces, vpart, ei, energy);
   }
 }
