@@ -93,20 +93,21 @@ __device__ __forceinline__ void sched_init(const Sched& sc, SchedState& st) {
 
 // A row-major [rows][cols] global matrix (cols a multiple of 4) into LDS with
 // row stride ld, by the whole workgroup: 16-byte loads when the source allows.
-__device__ __forceinline__ void stage_rows(float* lds, int ld, const float* __restrict__ g, int rows, int cols) {
+__device__ __forceinline__ void stage_rows(float* lds, int ld, const float* __restrict__ g, int rows, int cols,
+                                           float scale = 1.f) {
   if ((reinterpret_cast<uintptr_t>(g) & 15) == 0) {
     const float4* g4 = reinterpret_cast<const float4*>(g);
     const int n4 = rows * cols / 4;
     for (int k = threadIdx.x; k < n4; k += blockDim.x) {
       const float4 v = g4[k];
       float* d = lds + ((4 * k) / cols) * ld + (4 * k) % cols;
-      d[0] = v.x;
-      d[1] = v.y;
-      d[2] = v.z;
-      d[3] = v.w;
+      d[0] = v.x * scale;
+      d[1] = v.y * scale;
+      d[2] = v.z * scale;
+      d[3] = v.w * scale;
     }
   } else {
-    for (int k = threadIdx.x; k < rows * cols; k += blockDim.x) lds[(k / cols) * ld + k % cols] = g[k];
+    for (int k = threadIdx.x; k < rows * cols; k += blockDim.x) lds[(k / cols) * ld + k % cols] = g[k] * scale;
   }
 }
 
@@ -189,6 +190,48 @@ __device__ __forceinline__ void silu_tiles(const f32x16 z[2], f32x16 s[2]) {
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[m][r] = silu(z[m][r]);
+}
+
+// The chain with the first layer's weights scaled by KEXP = -log2(e) (the
+// one-species folded kernels stage KEXP W1): z1' = KEXP z1, so 2^{z'} = e^{-z}
+// enters the sigmoid with no multiply, and s' = z' sigma(z) = KEXP silu(z)
+// carries the same factor into the next layer (z2' = s1' W2 = KEXP z2) and on
+// into T.  The derivative sigma + (s' / KEXP)(1 - sigma) = silu'(z) is
+// unscaled.  Two vector instructions fewer per unit with its derivative, one
+// without.
+constexpr float KEXP = -1.44269504088896341f;
+constexpr float KEXP_INV2 = 0.480453013918201424667f;  // 1 / KEXP^2 = (ln 2)^2
+__device__ __forceinline__ float sigmoid_kexp(float zs) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(zs));
+}
+
+__device__ __forceinline__ void silu_and_deriv_kexp(const f32x16 z[2], f32x16 s[2], f32x16 d[2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float zz = z[m][r], sg = sigmoid_kexp(zz), ss = zz * sg;
+      s[m][r] = ss;
+      float dd = fmaf(fmaf(-sg, ss, ss), 1.f / KEXP, sg);
+      asm volatile("" : "+v"(dd));
+      d[m][r] = dd;
+    }
+}
+
+__device__ __forceinline__ void silu_tiles_kexp(const f32x16 z[2], f32x16 s[2]) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[m][r] = z[m][r] * sigmoid_kexp(z[m][r]);
+}
+
+template <bool K>
+__device__ __forceinline__ void silu_and_deriv_t(const f32x16 z[2], f32x16 s[2], f32x16 d[2]) {
+  if (K) silu_and_deriv_kexp(z, s, d); else silu_and_deriv(z, s, d);
+}
+template <bool K>
+__device__ __forceinline__ void silu_tiles_t(const f32x16 z[2], f32x16 s[2]) {
+  if (K) silu_tiles_kexp(z, s); else silu_tiles(z, s);
 }
 
 // Geometry of the edge a lane works on (binary64, as the neighbour list).
@@ -276,8 +319,8 @@ struct Units {
 // W1 and W2 only (the reassociated kernels read the last layer from global memory).
 constexpr int W12_FLOATS = NB * LDH + HID * LDH;
 __device__ __forceinline__ void stage_w12(float* lds, const float* __restrict__ W1,
-                                          const float* __restrict__ W2, int p) {
-  stage_rows(lds, LDH, W1 + (size_t)p * NB * HID, NB, HID);
+                                          const float* __restrict__ W2, int p, float w1_scale = 1.f) {
+  stage_rows(lds, LDH, W1 + (size_t)p * NB * HID, NB, HID, w1_scale);
   stage_rows(lds + NB * LDH, LDH, W2 + (size_t)p * HID * HID, HID, HID);
 }
 

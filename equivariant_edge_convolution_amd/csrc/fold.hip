@@ -97,6 +97,7 @@ __device__ __forceinline__ float* stash_tile(float* zw, int q0, int qa) {
 // ------------------------------------------------------------------ forward
 // One 32-edge tile [q0, q0 + 32) of a unit: T += s2^T Y over the tile.  With a
 // stash tile zs, also its rows (edge slot k at zs + k ZROW).
+template <bool K = false>
 __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const Recv& xi,
                                          const float* w1s, const float* w2s, float (*ysm)[NLM + 1],
                                          int q0, int qa, int qb, int s, int h, f32x4 T[4], float* zs) {
@@ -116,7 +117,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
   }
   if (zs != nullptr) {
     f32x16 d[2];
-    silu_and_deriv(z, a, d);  // s1 and silu'(z1), edges on N: hidden hid_k0(ks) + 4h
+    silu_and_deriv_t<K>(z, a, d);  // s1 and silu'(z1), edges on N: hidden hid_k0(ks) + 4h
     if (valid) {
       float* row = zs + s * ZROW + 4 * h;
 #pragma unroll
@@ -127,7 +128,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
               make_float4(d[m][4 * j], d[m][4 * j + 1], d[m][4 * j + 2], d[m][4 * j + 3]);
     }
   } else {
-    silu_tiles(z, a);  // s1, edges on N
+    silu_tiles_t<K>(z, a);  // s1, edges on N
   }
   // z2 with edges on M: register r of tile m = edge fperm(r) + 4h, hidden 32 m + s
   {
@@ -154,7 +155,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
       }
     }
   }
-  silu_tiles(z, a);  // s2, edges on M
+  silu_tiles_t<K>(z, a);  // s2, edges on M
   {
     float Y[16];
     sph16(g.ux, g.uy, g.uz, Y);
@@ -310,6 +311,7 @@ __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int 
 // One 32-edge tile of the backward of a unit: g = dE/dd of its edges.  The
 // geometry, silu'(z1) and z2 come from the stash tile zs when given, else are
 // recomputed.
+template <bool K = false>
 __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const int32_t* perm,
                                          const float* w1s, const float* w2s, float (*msm)[HID + 1],
                                          float (*ybsm)[NLM + 1], int q0, int qa, int qb, int s, int h,
@@ -338,7 +340,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
         d1[m][4 * j] = v1.x; d1[m][4 * j + 1] = v1.y; d1[m][4 * j + 2] = v1.z; d1[m][4 * j + 3] = v1.w;
         z[m][4 * j] = v2.x; z[m][4 * j + 1] = v2.y; z[m][4 * j + 2] = v2.z; z[m][4 * j + 3] = v2.w;
       }
-    silu_and_deriv(z, s2, d2);
+    silu_and_deriv_t<K>(z, s2, d2);
   } else {
     g = geo_from_raw(in, edge_raw(in, e), xi.x);
     sd = basis_seed(g.r, in.inv_rc, g.inv_r, h);
@@ -348,9 +350,9 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
       basis16f<false>(sd, in.inv_rc_f, h, bas, nullptr);
       layer1(w1s, bas, s, h, z);
     }
-    silu_and_deriv(z, s1, d1);
+    silu_and_deriv_t<K>(z, s1, d1);
     layer2(w2s, s1, s, h, z);
-    silu_and_deriv(z, s2, d2);
+    silu_and_deriv_t<K>(z, s2, d2);
   }
   __builtin_amdgcn_sched_barrier(0);
   // Ybar[edge][lm] = sum_k s2[edge][k] M[lm][k] on 16x16x4 tiles: swapping rows
@@ -536,10 +538,14 @@ __device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane
 // the waves' partials, in wave order) into tw, then wave w forms M for
 // harmonics 2w and 2w + 1 (lane = hidden unit k, G_l read from global memory
 // along rows: G is symmetric) into msh, and its share of E_i = 1/2 sum T.M
-// into esh[w].  Returns E_i (the shares in wave order) to every thread.
+// into esh[w].  Returns E_i (the shares in wave order) to every thread.  M and
+// E_i are multiplied by `scale` (1 / KEXP^2 when T carries the factor KEXP of
+// the scaled chain: M then carries 1 / KEXP, which the backward's scaled s2
+// cancels).
 template <int W, int TSM_OFF, int STRIDE>
 __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wbase, const float* __restrict__ G,
-                                                     int lane, int wave, float (*msh)[HID + 1], float* esh) {
+                                                     int lane, int wave, float (*msh)[HID + 1], float* esh,
+                                                     float scale = 1.f) {
   static_assert(W == 8, "two harmonics per wave");
   for (int e = threadIdx.x; e < HID * NLM; e += 64 * W) {
     float v = tw[e];
@@ -560,8 +566,8 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
     m0 += g0[kk * HID] * tsm[kk][lm0];
     m1 += g1[kk * HID] * tsm[kk][lm1];
   }
-  msh[lm0][lane] = m0;
-  msh[lm1][lane] = m1;
+  msh[lm0][lane] = m0 * scale;
+  msh[lm1][lane] = m1 * scale;
   float es = tsm[lane][lm0] * m0 + tsm[lane][lm1] * m1;
   for (int off = 32; off > 0; off >>= 1) es += __shfl_xor(es, off);
   if (lane == 0) esh[wave] = es;
@@ -569,7 +575,7 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
   float e = 0.f;
 #pragma unroll
   for (int w = 0; w < W; ++w) e += esh[w];
-  return 0.5f * e;
+  return 0.5f * e * scale;
 }
 
 // ------------------------------------------------------------------ fused (one species)
@@ -644,7 +650,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   float* gs = wl + W12_FLOATS;
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  stage_w12(wl, W1, W2, 0);
+  stage_w12(wl, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
   for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) gs[(t >> 6) * LDG + (t & 63)] = G[t];
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
@@ -659,7 +665,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     const Recv xi = recv_pos(in, i);
     float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
     for (int q0 = qa; q0 < qb; q0 += 32)
-      fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
+      fwd_tile<true>(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, stash_tile(zw, q0, qa));
     // T block b register r, lane l: hidden 16 b + 4 (l / 16) + r, harmonic l % 16
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -670,14 +676,14 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     float macc[NLM];
     const float* g = gs + lane * LDG;
     const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return g[l * HID * LDG + kk]; }, macc);
-    if (lane == 0) ei[i] = e2;
+    if (lane == 0) ei[i] = e2 * KEXP_INV2;  // T carries KEXP
     if (qb <= qa) continue;
     wave_sync_lds();  // msm overlays tsm
 #pragma unroll
-    for (int lm = 0; lm < NLM; ++lm) L.msm[lm][lane] = macc[lm];
+    for (int lm = 0; lm < NLM; ++lm) L.msm[lm][lane] = macc[lm] * KEXP_INV2;  // M / KEXP
     wave_sync_lds();
     for (int q0 = qa; q0 < qb; q0 += 32)
-      bwd_tile(in, xi, nullptr, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
+      bwd_tile<true>(in, xi, nullptr, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, stash_tile(zw, q0, qa));
   }
 }
 
@@ -703,7 +709,7 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   const float* w1s = w12;
   const float* w2s = w12 + NB * LDH;
   const int N = un.n_atoms;
-  stage_w12(w12, W1, W2, 0);
+  stage_w12(w12, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
   __syncthreads();
   float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
   for (int i = blockIdx.x; i < N; i += gridDim.x) {
@@ -716,7 +722,7 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     for (int b = 0; b < 4; ++b) T[b] = zero4();
     int j = 0;
     for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      fwd_tile(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
+      fwd_tile<true>(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
                j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -725,13 +731,13 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     __syncthreads();
     {
       const float e2 = gram_epilogue_split<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(
-          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh, esh);
+          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh, esh, KEXP_INV2);
       if (threadIdx.x == 0) ei[i] = e2;
     }
     __syncthreads();
     j = 0;
     for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      bwd_tile(in, xi, nullptr, w1s, w2s, msh, L.ybsm, q0, qa, qb, s, h, gout,
+      bwd_tile<true>(in, xi, nullptr, w1s, w2s, msh, L.ybsm, q0, qa, qb, s, h, gout,
                j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
     __syncthreads();  // msh and the wave buffers are rewritten for the next receiver
   }
