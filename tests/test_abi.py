@@ -71,6 +71,14 @@ def test_host_side_errors():
                                  ctypes.byref(bad), ctypes.c_void_p(1024), None, ctypes.c_void_p(2048),
                                  None, ctypes.c_void_p(8192), 1 << 20)
         assert B.STATUS[st] == "EEC_ERR_SHAPE"
+    # edge counts past the int32 index range (E <= 2^31 - 1) and negative sizes
+    good = _model_struct()
+    for n_atoms, n_edges in ((4, 1 << 31), (-1, 0), (4, -1)):
+        gbig = B._Graph(n_atoms, n_edges, 4096, 4096, 4096, 4096)
+        st = L.eec_energy_forces(None, ctypes.byref(gbig), ctypes.c_void_p(256), box, ctypes.c_void_p(512),
+                                 ctypes.byref(good), ctypes.c_void_p(1024), None, ctypes.c_void_p(2048),
+                                 None, ctypes.c_void_p(8192), 1 << 20)
+        assert B.STATUS[st] == "EEC_ERR_SHAPE", (n_atoms, n_edges)
     # outputs overlapping inputs
     m = _model_struct(fake_ptr=1 << 20)
     st = L.eec_energy_forces(None, ctypes.byref(g), ctypes.c_void_p(1 << 16), box, ctypes.c_void_p(1 << 24),
