@@ -1134,16 +1134,24 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
     bstart[z + 1] = bstart[z] + (z < S ? (zstart[z + 1] - zstart[z] + W - 1) / W : 0);
   const int total = bstart[MULTI_MAX_S];
   float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
+  // the network runs the scaled chain (W1 staged as KEXP W1); p is uniform over
+  // the workgroup, and a pair already in LDS (the last backward species of one
+  // batch is the first forward species of the next) is not staged again
+  constexpr bool K = !TAB;
+  int loaded = -1;
   auto stage = [&](int p) {
-    if (TAB && !W3L) return;  // nothing to stage
+    if ((TAB && !W3L) || p == loaded) return;  // nothing to stage
     __syncthreads();
     if (TAB)
       stage_rows(wl + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
-    else if (W3L)
-      stage_weights<C>(wl, W1, W2, W3, p);
-    else
-      stage_w12(wl, W1, W2, p);
+    else if (W3L) {
+      stage_rows(wl + Lds<C>::W1, LDH, W1 + (size_t)p * NB * HID, NB, HID, KEXP);
+      stage_rows(wl + Lds<C>::W2, LDH, W2 + (size_t)p * HID * HID, HID, HID);
+      stage_rows(wl + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
+    } else
+      stage_w12(wl, W1, W2, p, KEXP);
     __syncthreads();
+    loaded = p;
   };
   for (int b = blockIdx.x; b < total; b += gridDim.x) {
     int z = 0;
@@ -1176,7 +1184,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
         if (TAB)
           fwd_tile_tab(in, un.perm, xi, tab_pair(ta, p), tpb[wave], L.ysm, q0, qa, qb, s, h, T, zs);
         else
-          fwd_tile(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, zs);
+          fwd_tile<K>(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, zs);
       }
       float as[CPL][NLM];
       if (W3L)
@@ -1190,7 +1198,10 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
         for (int k = 0; k < NLM; ++k) acc[q][k] += hc * as[q][k];
       }
     }
-    // E_i = sum_c w_c sum_lm A^2; acc becomes dE/dA = 2 w A
+    // E_i = sum_c w_c sum_lm A^2; acc becomes dE/dA = 2 w A.  With the scaled
+    // chain acc = KEXP A: E_i takes 1 / KEXP^2, and dE/dA is kept as
+    // 2 w A / KEXP, which the backward's scaled s2 cancels.
+    constexpr float KS = K ? KEXP_INV2 : 1.f;
     float esum = 0.f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -1199,10 +1210,11 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
 #pragma unroll
       for (int k = 0; k < NLM; ++k) {
         sq += acc[q][k] * acc[q][k];
-        acc[q][k] *= 2.f * wc;
+        acc[q][k] *= 2.f * wc * KS;
       }
       esum += wc * sq;
     }
+    esum *= KS;
     for (int off = 32; off > 0; off >>= 1) esum += __shfl_xor(esum, off);
     if (valid && lane == 0) ei[i] = esum;
     // backward in reverse species order: the last forward species' weights are
@@ -1234,7 +1246,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
         if (TAB)
           bwd_tile_tab(in, xi, un.perm, tab_pair(ta, p), L.msm, L.ybsm, q0, qa, qb, s, h, gout, zs);
         else
-          bwd_tile(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, zs);
+          bwd_tile<K>(in, xi, un.perm, w1s, w2s, L.msm, L.ybsm, q0, qa, qb, s, h, gout, zs);
       }
     }
   }
