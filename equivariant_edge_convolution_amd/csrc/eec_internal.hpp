@@ -13,6 +13,7 @@ enum : uint32_t {
   FLAG_OUT_OF_BOX = 1u,
   FLAG_SPECIES = 2u,
   FLAG_GEOMETRY = 4u,
+  FLAG_SLOT_OVERFLOW = 8u,  // a row longer than NB_SLOT_CAP (builder-internal)
 };
 
 struct Box {
@@ -26,8 +27,10 @@ struct NbPlan {
   size_t bytes;
   // byte offsets into the workspace
   size_t off_cell_count, off_cell_fill, off_cell_start, off_cell_atoms, off_cell_of, off_cell_pos, off_deg,
-      off_scratch;
+      off_scratch, off_slots;
 };
+// Key slots per atom of the builder's counting fill (N * NB_SLOT_CAP * 4 bytes of workspace).
+constexpr int NB_SLOT_CAP = 256;
 NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff);
 
 // Runs the whole builder; returns EEC_OK / error.  Writes *n_edges.

@@ -224,61 +224,61 @@ __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const doub
   }
 }
 
-__global__ void __launch_bounds__(256) k_nb_count(int32_t n, Grid gr, const double* __restrict__ pos,
-                                                  const int32_t* __restrict__ cell_of,
-                                                  const int32_t* __restrict__ cell_start,
-                                                  const int32_t* __restrict__ cell_atoms,
-                                                  const double* __restrict__ cell_pos,
-                                                  uint32_t* __restrict__ deg,
-                                                  uint32_t* __restrict__ flags) {
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (i >= n) return;
-  uint32_t cnt = 0;
-  bool coincident = false;
-  for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, n - 1, lane,
-                 [&](bool keep, int, int, double r2) {
-                   cnt += keep ? 1u : 0u;
-                   coincident |= keep && (r2 == 0.0);
-                 });
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if (coincident) atomicOr(flags, FLAG_GEOMETRY);
-  if (lane == 0) deg[i] = cnt;
-}
-
-// Writes the unsorted (j * 27 + s) keys of each row into `keys` at its CSR slots.
+// Writes the unsorted (j * 27 + s) keys of each row.  SLOTS (the first pass,
+// before any row offsets exist): row i's keys go to its NB_SLOT_CAP slots at
+// keys + i * NB_SLOT_CAP and its degree to deg[i]; a row longer than its slots
+// (the keys past them dropped, the degree whole) raises FLAG_SLOT_OVERFLOW,
+// and the host then runs the second form, which writes every row's keys at
+// its CSR positions keys + rp[i].
+template <bool SLOTS>
 __global__ void __launch_bounds__(256) k_nb_fill(int32_t n, Grid gr, const double* __restrict__ pos,
                                                  const int32_t* __restrict__ cell_of,
                                                  const int32_t* __restrict__ cell_start,
                                                  const int32_t* __restrict__ cell_atoms,
                                                  const double* __restrict__ cell_pos,
                                                  const int32_t* __restrict__ rp,
-                                                 int32_t* __restrict__ keys) {
+                                                 int32_t* __restrict__ keys, uint32_t* __restrict__ deg,
+                                                 uint32_t* __restrict__ flags) {
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
-  int base = rp[i];
-  const int end = rp[i + 1];
+  const int64_t base0 = SLOTS ? (int64_t)i * NB_SLOT_CAP : (int64_t)rp[i];
+  const int64_t end = SLOTS ? base0 + NB_SLOT_CAP : (int64_t)rp[i + 1];
+  int64_t base = base0;
+  bool coincident = false;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for_candidates(i, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, n - 1, lane,
-                 [&](bool keep, int j, int s, double) {
+                 [&](bool keep, int j, int s, double r2) {
                    const uint64_t mask = __ballot(keep);
-                   const int at = base + __popcll(mask & below);
+                   const int64_t at = base + __popcll(mask & below);
                    if (keep && at < end) keys[at] = j * 27 + s;
                    base += __popcll(mask);
+                   if (SLOTS) coincident |= keep && (r2 == 0.0);
                  });
+  if (SLOTS) {
+    const int64_t cnt = base - base0;
+    if (coincident) atomicOr(flags, FLAG_GEOMETRY);
+    if (lane == 0) {
+      deg[i] = (uint32_t)cnt;
+      if (cnt > NB_SLOT_CAP) atomicOr(flags, FLAG_SLOT_OVERFLOW);
+    }
+  }
 }
 
 // One 64-thread workgroup per row: rank-sort the row's distinct keys and
 // write the sorted senders and image shifts.
+// With `slots`, row i's keys are read from slots + i * NB_SLOT_CAP (every row
+// then has at most NB_SLOT_CAP keys), else from keys + rp[i].
 __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __restrict__ rp,
-                                                const int32_t* __restrict__ keys,
+                                                const int32_t* __restrict__ keys_csr,
+                                                const int32_t* __restrict__ slots,
                                                 int32_t* __restrict__ col, int8_t* __restrict__ shift) {
   __shared__ int32_t sk[SORT_LDS];
   const int i = blockIdx.x;
   const int lane = threadIdx.x;
   if (i >= n) return;
   const int a = rp[i], deg = rp[i + 1] - a;
+  const int32_t* row = slots != nullptr ? slots + (int64_t)i * NB_SLOT_CAP : keys_csr + a;  // the row's keys
   auto emit = [&](int r, int32_t key) {
     const int s = key % 27;
     col[a + r] = key / 27;
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
     // 4 or more apart across lanes (shuffles), closer pairs within a lane
     int32_t v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = 4 * lane + r < deg ? keys[a + 4 * lane + r] : INT32_MAX;
+    for (int r = 0; r < 4; ++r) v[r] = 4 * lane + r < deg ? row[4 * lane + r] : INT32_MAX;
     for (int k = 2; k <= 256; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
         if (jj >= 4) {
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
     // bitonic sort of the keys padded to a power of two (the pads sort last)
     int np2 = 64;
     while (np2 < deg) np2 <<= 1;
-    for (int k = lane; k < np2; k += 64) sk[k] = k < deg ? keys[a + k] : INT32_MAX;
+    for (int k = lane; k < np2; k += 64) sk[k] = k < deg ? row[k] : INT32_MAX;
     __syncthreads();
     for (int k = 2; k <= np2; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
     }
     for (int k = lane; k < deg; k += 64) emit(k, sk[k]);
   } else {
-    const int32_t* src = keys + a;
+    const int32_t* src = row;
     for (int k = lane; k < deg; k += 64) {
       const int32_t key = src[k];
       int rank = 0;
@@ -473,6 +473,7 @@ NbPlan nb_plan(int32_t n_atoms, const double* box, double cutoff) {
   p.off_cell_pos = o;   o += align256(3 * sizeof(double) * std::max<int64_t>(N, 1));
   p.off_deg = o;        o += align256(sizeof(uint32_t) * (N + 1) + sizeof(int32_t) * (N + 1));
   p.off_scratch = o;    o += 256;
+  p.off_slots = o;      o += align256(sizeof(int32_t) * NB_SLOT_CAP * std::max<int64_t>(N, 1));
   p.bytes = o;
   return p;
 }
@@ -502,10 +503,14 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   }
   k_scan_excl<<<1, 1024, 0, s>>>(cell_count, nc, cell_start, nullptr);
   Grid gr{p.nc[0], p.nc[1], p.nc[2], box[0], box[1], box[2], cutoff * cutoff};
+  // One pass over the candidates into per-atom key slots that also counts the
+  // rows; only when a row outgrows its slots does a second pass fill the keys
+  // at the CSR positions.
+  int32_t* slots = (int32_t*)(ws + p.off_slots);
   if (n > 0) {
     k_cell_place<<<blocks_for(n, 256), 256, 0, s>>>(n, pos, cell_of, cell_start, cell_fill, cell_atoms, cell_pos);
-    k_nb_count<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, deg,
-                                                 flags);
+    k_nb_fill<true><<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos,
+                                                      nullptr, slots, deg, flags);
   }
   k_scan_excl<<<1, 1024, 0, s>>>(deg, n, rp_tmp, total);
   // The flags and the edge total come back through a 16-byte pinned host word
@@ -539,9 +544,13 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
 
   k_copy_i32<<<blocks_for(n + 1, 256), 256, 0, s>>>(rp_tmp, row_ptr, n + 1);
   if (n > 0 && host.total > 0) {
-    k_nb_fill<<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos, row_ptr,
-                                                rev /* keys staged here */);
-    k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, rev, col, shift);
+    if (host.flags & FLAG_SLOT_OVERFLOW) {
+      k_nb_fill<false><<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos,
+                                                         row_ptr, rev /* keys staged here */, nullptr, nullptr);
+      k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, rev, nullptr, col, shift);
+    } else {
+      k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, nullptr, slots, col, shift);
+    }
     k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev, flags);
   }
   if (hipGetLastError() != hipSuccess) { *why = "kernel launch failed"; return EEC_ERR_HIP; }

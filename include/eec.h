@@ -133,6 +133,9 @@ typedef struct {
  *              EEC_ERR_CAPACITY (then it is the capacity required and the CSR
  *              arrays are not written).
  *   workspace  >= eec_neighbors_workspace_bytes(n_atoms, box, cutoff) bytes
+ *              (about 1.1 KB per atom: the cell list and 256 key slots per
+ *              atom for the counting pass; rows longer than 256 edges take a
+ *              second pass over the candidates)
  * Synchronises `stream` once (to read E and the validity flags, through a
  * 16-byte pinned host word that the library allocates on a thread's first
  * call and keeps); the CSR arrays are written after that, on `stream`, so
