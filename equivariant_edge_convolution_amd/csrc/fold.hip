@@ -186,9 +186,27 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
   wave_sync_lds();
 }
 
+// The multi-species kernel's LDS copy of W3 (C = 64): W3I[k][c][l] = W3[k][l C + c],
+// the four degrees of a channel in one 16-byte word, rows of W3I_LD floats
+// (a multiple of 4; 260 mod 64 = 4, so a wave reading one word per row or one
+// per channel touches every bank once per 16 lanes).
+constexpr int W3I_LD = 4 * 64 + 4;
+constexpr int W3I_FLOATS = HID * W3I_LD;
+
+// Stages W3[p] into the interleaved layout.
+__device__ __forceinline__ void stage_w3i(float* lds, const float* __restrict__ W3p) {
+  constexpr int C = 64;
+  for (int t = threadIdx.x; t < HID * C; t += blockDim.x) {
+    const int k = t / C, c = t % C;
+    const float* src = W3p + (size_t)k * 4 * C + c;
+    *reinterpret_cast<float4*>(lds + k * W3I_LD + 4 * c) = make_float4(src[0], src[C], src[2 * C], src[3 * C]);
+  }
+}
+
 // T of the unit to LDS, then acc[q][lm] = sum_k T[k][lm] W3[k][l(lm) C + c]
 // for channel c = lane + 64 q (the h_c factor is the caller's).  W3[k][j] is
-// w3[k * SK + j] (global memory: SK = 4 C; LDS: its padded row stride).
+// w3[k * SK + j] (global memory: SK = 4 C), or SK = 0: the interleaved LDS
+// copy W3I (C = 64).
 template <int C, int SK>
 __device__ __forceinline__ void unit_last_layer(const f32x4 T[4], float (*tsm)[NLM], const float* w3,
                                                 int lane, float acc[C / 64][NLM]) {
@@ -213,8 +231,14 @@ __device__ __forceinline__ void unit_last_layer(const f32x4 T[4], float (*tsm)[N
     }
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      const float* wr = w3 + (size_t)k * SK + lane + 64 * q;
-      const float w0 = wr[0], wl1 = wr[C], wl2 = wr[2 * C], wl3 = wr[3 * C];
+      float w0, wl1, wl2, wl3;
+      if (SK == 0) {  // the interleaved LDS copy: W3I[k][c][l], rows of W3I_LD floats
+        const float4 w = *reinterpret_cast<const float4*>(w3 + (size_t)k * W3I_LD + 4 * (lane + 64 * q));
+        w0 = w.x; wl1 = w.y; wl2 = w.z; wl3 = w.w;
+      } else {
+        const float* wr = w3 + (size_t)k * SK + lane + 64 * q;
+        w0 = wr[0]; wl1 = wr[C]; wl2 = wr[2 * C]; wl3 = wr[3 * C];
+      }
       acc[q][0] += t[0] * w0;
 #pragma unroll
       for (int lm = 1; lm < 4; ++lm) acc[q][lm] += t[lm] * wl1;
@@ -277,8 +301,8 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
 // ------------------------------------------------------------------ backward
 // M[lm][k] = sum_c (dE/dA h)[lm][c] W3[k][l(lm) C + c] from the staged ahsm rows
 // (lane = hidden k), into msm over the ahsm region.  W3[k][j] of this lane's k
-// is wt[j * SJ] (the transposed copy in global memory: SJ = 64; the LDS copy:
-// wt = its row k, SJ = 1).
+// is wt[j * SJ] (the transposed copy in global memory: SJ = 64), or SJ = 0:
+// wt = row k of the interleaved LDS copy W3I (C = 64).
 template <int C, int SJ>
 __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int lane, float (*msm)[HID + 1]) {
   float macc[NLM];
@@ -292,8 +316,14 @@ __device__ __forceinline__ void unit_M(float (*ahsm)[AHS], const float* wt, int 
       const float4 x = *reinterpret_cast<const float4*>(&ahsm[c][4 * v]);
       av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
     }
-    const float w0 = wt[(size_t)c * SJ], wl1 = wt[(size_t)(C + c) * SJ];
-    const float wl2 = wt[(size_t)(2 * C + c) * SJ], wl3 = wt[(size_t)(3 * C + c) * SJ];
+    float w0, wl1, wl2, wl3;
+    if (SJ == 0) {  // the interleaved LDS copy, wt = row k of W3I
+      const float4 w = *reinterpret_cast<const float4*>(wt + 4 * c);
+      w0 = w.x; wl1 = w.y; wl2 = w.z; wl3 = w.w;
+    } else {
+      w0 = wt[(size_t)c * SJ]; wl1 = wt[(size_t)(C + c) * SJ];
+      wl2 = wt[(size_t)(2 * C + c) * SJ]; wl3 = wt[(size_t)(3 * C + c) * SJ];
+    }
     macc[0] += av[0] * w0;
 #pragma unroll
     for (int lm = 1; lm < 4; ++lm) macc[lm] += av[lm] * wl1;
@@ -1106,7 +1136,8 @@ constexpr int MULTI_MAX_S = 3;
 template <int C, bool W3L>
 struct MultiLds {
   static constexpr int PW = FoldLds<C>::BWD_ONLY > FoldLds<C>::FWD_ONLY ? FoldLds<C>::BWD_ONLY : FoldLds<C>::FWD_ONLY;
-  static constexpr int WEIGHTS = W3L ? Lds<C>::FLOATS : W12_FLOATS;
+  static constexpr int W3I = W12_FLOATS;  // the interleaved W3 after W1 and W2
+  static constexpr int WEIGHTS = W3L ? W12_FLOATS + W3I_FLOATS : W12_FLOATS;
 };
 
 // TAB: s2 and ds2/dr of each sender species' pair from the radial tables (only
@@ -1118,6 +1149,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
              const float* __restrict__ W3T, const float* __restrict__ emb, const float* __restrict__ w_read,
              TabArgs ta, float* __restrict__ ei, float* __restrict__ gout, float* __restrict__ stash) {
   constexpr int NC = 4 * C, CPL = C / 64;
+  static_assert(!W3L || C == 64, "the interleaved LDS copy of W3 is laid out for 64 channels");
   __shared__ float wl[MultiLds<C, W3L>::WEIGHTS];
   __shared__ __align__(16) float wbuf[W][MultiLds<C, W3L>::PW];
   __shared__ float4 tpb[W][32];
@@ -1143,11 +1175,10 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
     if ((TAB && !W3L) || p == loaded) return;  // nothing to stage
     __syncthreads();
     if (TAB)
-      stage_rows(wl + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
+      stage_w3i(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
     else if (W3L) {
-      stage_rows(wl + Lds<C>::W1, LDH, W1 + (size_t)p * NB * HID, NB, HID, KEXP);
-      stage_rows(wl + Lds<C>::W2, LDH, W2 + (size_t)p * HID * HID, HID, HID);
-      stage_rows(wl + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
+      stage_w12(wl, W1, W2, p, KEXP);
+      stage_w3i(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
     } else
       stage_w12(wl, W1, W2, p, KEXP);
     __syncthreads();
@@ -1188,7 +1219,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
       }
       float as[CPL][NLM];
       if (W3L)
-        unit_last_layer<C, Lds<C>::LD3>(T, L.tsm, wl + Lds<C>::W3, lane, as);
+        unit_last_layer<C, 0>(T, L.tsm, wl + MultiLds<C, W3L>::W3I, lane, as);
       else
         unit_last_layer<C, NC>(T, L.tsm, W3 + (size_t)p * HID * NC, lane, as);
 #pragma unroll
@@ -1238,7 +1269,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
       }
       wave_sync_lds();
       if (W3L)
-        unit_M<C, 1>(L.ahsm, wl + Lds<C>::W3 + lane * Lds<C>::LD3, lane, L.msm);
+        unit_M<C, 0>(L.ahsm, wl + MultiLds<C, W3L>::W3I + lane * W3I_LD, lane, L.msm);
       else
         unit_M<C, HID>(L.ahsm, W3T + (size_t)p * NC * HID + lane, lane, L.msm);
       for (int q0 = qa; q0 < qb; q0 += 32, ++t) {
