@@ -532,7 +532,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
 }
 
 // M_i and E_i from the staged T of the unit through the Gram matrices (lane =
-// hidden k).  G_l[k][k'] is read as g(l, k') for this lane's k.
+// hidden k).  g(k') returns G_0..G_3[k][k'] for this lane's k.
 template <typename GF>
 __device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane, GF&& g, float macc[NLM]) {
 #pragma unroll
@@ -545,7 +545,8 @@ __device__ __forceinline__ float gram_epilogue(const float (*tsm)[NLM], int lane
       const float4 x = *reinterpret_cast<const float4*>(&tsm[kk][4 * v]);
       t[4 * v] = x.x; t[4 * v + 1] = x.y; t[4 * v + 2] = x.z; t[4 * v + 3] = x.w;
     }
-    const float g0 = g(0, kk), g1 = g(1, kk), g2 = g(2, kk), g3 = g(3, kk);
+    const float4 gv = g(kk);
+    const float g0 = gv.x, g1 = gv.y, g2 = gv.z, g3 = gv.w;
     macc[0] += g0 * t[0];
 #pragma unroll
     for (int lm = 1; lm < 4; ++lm) macc[lm] += g1 * t[lm];
@@ -617,9 +618,20 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
 //   G_l[k][k'] = sum_c 2 w_c h_c^2 W3[k][lC+c] W3[k'][lC+c]     (k_gram, per call)
 // give M_{lm} = G_{l(lm)} T_{lm} and E_i = 1/2 sum_lm T_{lm} . M_{lm}: one
 // 64 x 64 contraction per harmonic per receiver, whatever C is, instead of A
-// (16 x 64 x C) and M (16 x C x 64).  G (64 KB) sits in LDS beside W1 and W2.
-constexpr int LDG = HID + 1;                       // row stride of G_l in LDS
-constexpr int GRAM_FLOATS = 4 * HID * LDG;
+// (16 x 64 x C) and M (16 x C x 64).  G (64 KB) sits in LDS beside W1 and W2,
+// interleaved by degree: GI[k][k'][l] = G_l[k][k'], the four degrees of an
+// entry in one 16-byte word, rows of GI_LD floats (a multiple of 4; 260 mod
+// 64 = 4, so 16 lanes reading one word each from rows k touch every bank once).
+constexpr int GI_LD = 4 * HID + 4;
+constexpr int GRAM_FLOATS = HID * GI_LD;
+
+// G in global memory ([l][k][k']) into the interleaved LDS layout.
+__device__ __forceinline__ void stage_gram(float* gs, const float* __restrict__ G) {
+  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) {
+    const int l = t >> 12, k = (t >> 6) & 63, kk = t & 63;
+    gs[k * GI_LD + 4 * kk + l] = G[t];
+  }
+}
 
 // G_l[k][k'] for one species pair.  Block (l, four rows k): the degree-l
 // columns of W3 (64 x C) in LDS (16-byte loads where W3 allows, all issued
@@ -671,7 +683,7 @@ __global__ void __launch_bounds__(64 * W)
 k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
              const float* __restrict__ G, float* __restrict__ ei, float* __restrict__ gout,
              float* __restrict__ stash) {
-  __shared__ float wl[W12_FLOATS + GRAM_FLOATS];
+  __shared__ __align__(16) float wl[W12_FLOATS + GRAM_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
@@ -681,7 +693,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
   stage_w12(wl, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
-  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) gs[(t >> 6) * LDG + (t & 63)] = G[t];
+  stage_gram(gs, G);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
@@ -704,8 +716,9 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     wave_sync_lds();
     // M[lm][k] = sum_k' G_l(lm)[k][k'] T[k'][lm] and E_i = 1/2 sum T M (lane = hidden k)
     float macc[NLM];
-    const float* g = gs + lane * LDG;
-    const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return g[l * HID * LDG + kk]; }, macc);
+    const float* g = gs + lane * GI_LD;
+    const float e2 = gram_epilogue(L.tsm, lane, [&](int kk) { return *reinterpret_cast<const float4*>(g + 4 * kk); },
+                                   macc);
     if (lane == 0) ei[i] = e2 * KEXP_INV2;  // T carries KEXP
     if (qb <= qa) continue;
     wave_sync_lds();  // msm overlays tsm
@@ -1079,14 +1092,14 @@ template <int C, int W>
 __global__ void __launch_bounds__(64 * W)
 k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float* __restrict__ ei,
              float* __restrict__ gout, float* __restrict__ stash) {
-  __shared__ float gs[GRAM_FLOATS];
+  __shared__ __align__(16) float gs[GRAM_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   __shared__ float4 tpb[W][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) gs[(t >> 6) * LDG + (t & 63)] = G[t];
+  stage_gram(gs, G);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
@@ -1107,8 +1120,9 @@ k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float
       for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
     wave_sync_lds();
     float macc[NLM];
-    const float* g = gs + lane * LDG;
-    const float e2 = gram_epilogue(L.tsm, lane, [&](int l, int kk) { return g[l * HID * LDG + kk]; }, macc);
+    const float* g = gs + lane * GI_LD;
+    const float e2 = gram_epilogue(L.tsm, lane, [&](int kk) { return *reinterpret_cast<const float4*>(g + 4 * kk); },
+                                   macc);
     if (lane == 0) ei[i] = e2;
     if (qb <= qa) continue;
     wave_sync_lds();  // msm overlays tsm
@@ -1150,7 +1164,7 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
              TabArgs ta, float* __restrict__ ei, float* __restrict__ gout, float* __restrict__ stash) {
   constexpr int NC = 4 * C, CPL = C / 64;
   static_assert(!W3L || C == 64, "the interleaved LDS copy of W3 is laid out for 64 channels");
-  __shared__ float wl[MultiLds<C, W3L>::WEIGHTS];
+  __shared__ __align__(16) float wl[MultiLds<C, W3L>::WEIGHTS];
   __shared__ __align__(16) float wbuf[W][MultiLds<C, W3L>::PW];
   __shared__ float4 tpb[W][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
