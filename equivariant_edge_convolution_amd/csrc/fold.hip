@@ -733,9 +733,12 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
 // ------------------------------------------------------------------ split (one species, few receivers)
 // With fewer receivers than the chip has wave slots, one wave per receiver
 // leaves most CUs idle and one receiver's tiles in sequence are the whole
-// call.  Here a workgroup takes a receiver and its W waves share the row's
-// tiles (wave w: tiles w, w + W, ...): each sums its partial T, the first wave
-// adds them up in LDS and forms M and E_i from G in global memory (G is
+// call.  Here a workgroup takes two receivers at a time (i and i + gridDim.x)
+// and its W waves share their tiles, in one list (the first receiver's, then
+// the second's; wave w: tiles w, w + W, ...): five tiles a receiver fill eight
+// waves better in pairs than alone (no SIMD runs three tiles where one runs
+// one).  Each wave sums its partial T of each receiver into LDS; the readout
+// adds them up per receiver and forms M and E_i from G in global memory (G is
 // symmetric, so lane k reads G_l[k'][k] along a row), and every wave runs the
 // backward of its own tiles from its own stash rows.
 template <int C, int W>
@@ -745,7 +748,8 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
              float* __restrict__ stash) {
   __shared__ float w12[W12_FLOATS];
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
-  __shared__ __align__(16) float msh[NLM][HID + 1];  // M of the receiver, read by every wave
+  __shared__ __align__(16) float tsm2[W][HID * NLM];  // the waves' partial T of the second receiver
+  __shared__ __align__(16) float msh[2][NLM][HID + 1];  // M of the two receivers, read by every wave
   __shared__ float esh[W];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
@@ -755,34 +759,63 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   stage_w12(w12, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
   __syncthreads();
   float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
-  for (int i = blockIdx.x; i < N; i += gridDim.x) {
-    int s = lane & 31, h = lane >> 5;
-    asm volatile("" : "+v"(s), "+v"(h));
-    const int qa = un.row_ptr[i], qb = un.row_ptr[i + 1];
-    const Recv xi = recv_pos(in, i);
-    f32x4 T[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) T[b] = zero4();
-    int j = 0;
-    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      fwd_tile<true>(in, nullptr, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T,
-               j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+  // T block b register r, lane l: hidden 16 b + 4 (l / 16) + r, harmonic l % 16
+  auto put_t = [&](const f32x4 T[4], float* dst) {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) L.tsm[16 * b + 4 * (lane >> 4) + r][lane & 15] = T[b][r];
+      for (int r = 0; r < 4; ++r) dst[(16 * b + 4 * (lane >> 4) + r) * NLM + (lane & 15)] = T[b][r];
+  };
+  for (int i0 = blockIdx.x; i0 < N; i0 += 2 * gridDim.x) {
+    int s = lane & 31, h = lane >> 5;
+    asm volatile("" : "+v"(s), "+v"(h));
+    const int i1 = i0 + gridDim.x;
+    const int qa[2] = {un.row_ptr[i0], i1 < N ? un.row_ptr[i1] : 0};
+    const int qb[2] = {un.row_ptr[i0 + 1], i1 < N ? un.row_ptr[i1 + 1] : 0};
+    const int n0 = (qb[0] - qa[0] + 31) >> 5, n1 = (qb[1] - qa[1] + 31) >> 5;
+    const Recv xi[2] = {recv_pos(in, i0), recv_pos(in, i1 < N ? i1 : i0)};
+    f32x4 T[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) T[b] = zero4();
+    int cur = 0, j = 0;
+    for (int t = wave; t < n0 + n1; t += W, ++j) {
+      const int r = t < n0 ? 0 : 1;
+      if (r != cur) {  // the first receiver's partial is complete
+        put_t(T, &L.tsm[0][0]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) T[b] = zero4();
+        cur = 1;
+      }
+      const int q0 = qa[r] + 32 * (r ? t - n0 : t);
+      fwd_tile<true>(in, nullptr, xi[r], w1s, w2s, L.ysm, q0, qa[r], qb[r], s, h, T,
+                     j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+    }
+    if (cur == 0) {
+      put_t(T, &L.tsm[0][0]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) T[b] = zero4();
+    }
+    if (i1 < N) put_t(T, tsm2[wave]);
     __syncthreads();
     {
       const float e2 = gram_epilogue_split<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(
-          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh, esh, KEXP_INV2);
-      if (threadIdx.x == 0) ei[i] = e2;
+          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh[0], esh, KEXP_INV2);
+      if (threadIdx.x == 0) ei[i0] = e2;
+    }
+    if (i1 < N) {
+      const float e2 = gram_epilogue_split<W, 0, HID * NLM>(&tsm2[0][0], &tsm2[0][0], G, lane, wave, msh[1], esh,
+                                                            KEXP_INV2);
+      if (threadIdx.x == 0) ei[i1] = e2;
     }
     __syncthreads();
     j = 0;
-    for (int q0 = qa + 32 * wave; q0 < qb; q0 += 32 * W, ++j)
-      bwd_tile<true>(in, xi, nullptr, w1s, w2s, msh, L.ybsm, q0, qa, qb, s, h, gout,
-               j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
-    __syncthreads();  // msh and the wave buffers are rewritten for the next receiver
+    for (int t = wave; t < n0 + n1; t += W, ++j) {
+      const int r = t < n0 ? 0 : 1;
+      const int q0 = qa[r] + 32 * (r ? t - n0 : t);
+      bwd_tile<true>(in, xi[r], nullptr, w1s, w2s, msh[r], L.ybsm, q0, qa[r], qb[r], s, h, gout,
+                     j < STASH_TILES ? zw + (size_t)j * 32 * ZROW : nullptr);
+    }
+    __syncthreads();  // msh and the wave buffers are rewritten for the next pair
   }
 }
 
