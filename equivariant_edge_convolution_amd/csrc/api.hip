@@ -300,7 +300,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
       launch_gram(s, p, m, ws);
     } else {
       launch_prepare_rows(s, p, g, species, ws);
-      launch_transpose_w3(s, p, m, ws);
+      if (p.C != 64) launch_transpose_w3(s, p, m, ws);  // at C = 64 the kernel keeps W3 in LDS
     }
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);
@@ -340,7 +340,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     // one kernel per call from geometry to dE/dd, sender species after species
     mark(2 * EEC_PHASE_PREPARE);
     launch_prepare_rows(s, p, g, species, ws);
-    launch_transpose_w3(s, p, m, ws);
+    if (p.C != 64) launch_transpose_w3(s, p, m, ws);  // at C = 64 the kernel keeps W3 in LDS
     mark(2 * EEC_PHASE_PREPARE + 1);
     mark(2 * EEC_PHASE_FORWARD);
     launch_fold_multi(s, p, g, pos, b, m->cutoff, species, m, ei, gbuf, ws);

@@ -212,27 +212,46 @@ __global__ void __launch_bounds__(256) k_row_partition(int32_t n, int S, int64_t
 constexpr int SO_T = 1024;
 __global__ void __launch_bounds__(SO_T) k_species_order(int32_t n, int S, const int32_t* __restrict__ species,
                                                          int32_t* __restrict__ ord, int32_t* __restrict__ zstart) {
-  __shared__ int32_t cnt[4][SO_T + 1];
+  constexpr int NW = SO_T / 64;
+  __shared__ int32_t wsum[4][NW];
   __shared__ int32_t base[5];
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int per = (n + SO_T - 1) / SO_T;
   const int a = min(n, t * per), b = min(n, a + per);
   int c[4] = {0, 0, 0, 0};
   for (int k = a; k < b; ++k) c[min(max(species[k], 0), S - 1)]++;
-  for (int z = 0; z < S; ++z) cnt[z][t + 1] = c[z];
-  if (t < S) cnt[t][0] = 0;
+  // exclusive prefix of each species' count over the threads: inclusive scans
+  // inside each wave, then the wave totals in order
+  int incl[4];
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    int v = c[z];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    incl[z] = v;
+    if (lane == 63) wsum[z][wv] = v;
+  }
   __syncthreads();
-  if (t < S)
-    for (int k = 1; k <= SO_T; ++k) cnt[t][k] += cnt[t][k - 1];
+  if (t < 4) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int x = wsum[t][w];
+      wsum[t][w] = run;
+      run += x;
+    }
+    base[t + 1] = run;  // species t's total, made cumulative below
+  }
   __syncthreads();
   if (t == 0) {
     base[0] = 0;
-    for (int z = 0; z < S; ++z) base[z + 1] = base[z] + cnt[z][SO_T];
+    for (int z = 0; z < S; ++z) base[z + 1] += base[z];
     for (int z = 0; z <= S; ++z) zstart[z] = base[z];
   }
   __syncthreads();
   int pos[4];
-  for (int z = 0; z < S; ++z) pos[z] = base[z] + cnt[z][t];
+  for (int z = 0; z < S; ++z) pos[z] = base[z] + wsum[z][wv] + incl[z] - c[z];
   for (int k = a; k < b; ++k) ord[pos[min(max(species[k], 0), S - 1)]++] = k;
 }
 
