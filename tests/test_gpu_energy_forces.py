@@ -50,6 +50,29 @@ def test_energy_forces_elementwise(name, variant):
     assert np.abs(got["virial"] - W0).max() <= 1e-4 * np.abs(W0).max()
 
 
+@pytest.mark.parametrize("variant", ["folded", "tabulated"])
+@pytest.mark.parametrize("n_atoms", [300, 513])
+def test_split_kernel_ragged_receiver_pairs(n_atoms, variant):
+    # a random subset of a perturbed diamond cell (so no two atoms closer than
+    # the crystal's bond), one species: between 256 and 768 atoms the folded
+    # call runs one workgroup per two receivers (i, i + 256); 300 and 513 leave
+    # most workgroups with one receiver of the pair missing, and 513 a third
+    # receiver in a second pass
+    say(f"[energy_forces] split pairs, {n_atoms} atoms, {variant}")
+    base = I.make_config("D512" if n_atoms < 512 else "D1728")  # rows of about 3 and 2 tiles
+    keep = np.sort(np.random.default_rng(n_atoms).choice(base.n_atoms, n_atoms, replace=False))
+    cfg = I.make_cluster(base.pos[keep], base.box, seed=n_atoms)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    table = B.RadialTable(model, 6) if variant == "tabulated" else None
+    got = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, variant=variant,
+                                                   table=table).items()}
+    ref = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+
+
 _DENSE_REF = {}
 
 
