@@ -162,6 +162,7 @@ __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const doub
   // The first 64 members of three cells at a time, every load issued before
   // the tests; d = (x_j - x_i) + n L in binary64 as edge_vector forms it.
   constexpr int G = 3;
+  uint32_t big = 0;  // bit o: candidate cell o holds more than 64 atoms (wave-uniform)
 #pragma unroll
   for (int o0 = 0; o0 < 27; o0 += G) {
     int c2[G], s[G], sh[G][3], a[G], b[G], j[G];
@@ -172,6 +173,7 @@ __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const doub
       c2[u] = __builtin_amdgcn_readfirstlane(c2[u]);
       a[u] = cell_start[c2[u]];
       b[u] = cell_start[c2[u] + 1];
+      big |= (b[u] - a[u] > 64 ? 1u : 0u) << (o0 + u);
     }
     // loads from a valid slot in every lane (no load under a branch); lanes
     // past the cell's end are masked out below
@@ -197,8 +199,9 @@ __device__ __forceinline__ void for_candidates(int i, const Grid& gr, const doub
       f(keep, j[u], s[u], in_cell ? r2 : 1.0);
     }
   }
-  // members past the first 64 of a cell
-  for (int o = 0; o < 27; ++o) {
+  // members past the first 64 of the cells that have them
+  for (uint32_t m = big; m != 0; m &= m - 1) {
+    const int o = __builtin_ctz(m);
     int c2, s, shv[3];
     cell(o, c2, s, shv);
     const int ix = shv[0], iy = shv[1], iz = shv[2];
