@@ -10,11 +10,17 @@ reported as context).  Each timed step is one full energy/force call with
 every input already resident in device memory: radial network + message +
 readout + streaming backward + force scatter.
 
+Before the timed calls the headline variant runs untimed for at least
+--preload-ms of wall time (reported as "preload"), so that the clock has
+settled under load whatever --warmup asks for; then --warmup untimed calls,
+then --steps timed calls between two device synchronisations.
+
 The headline variant (--variant, default "folded") is eec_energy_forces_folded:
 the linear last radial layer applied once per receiver instead of once per
-edge (same outputs up to float32 rounding).  The other variant ("direct",
-eec_energy_forces: the radial weights R of every edge on matrix cores) is
-timed in the same run and reported under "variants".
+edge (same outputs up to float32 rounding).  The other variants ("direct",
+eec_energy_forces: the radial weights R of every edge on matrix cores;
+"tabulated": certified radial tables) are timed in the same run and reported
+under "variants".
 
 Also reported:
   roofline      the dominant kernel (one species, folded: the fused
@@ -25,13 +31,23 @@ Also reported:
                 against the FP32 matrix peak; `traffic` the HBM bytes per
                 launch from the recorded counter runs (recorded_traffic), or
                 null when the kernel has changed since they were taken;
+  call_ms       per-call device time (first to last kernel of a call, from the
+                hipEvents of a second pass of --steps calls): P50, P90, mean;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload
-                (all receivers of the cell: their forward and force backward),
-                on the host cores;
+                (its first receivers: their forward and force backward), median
+                of three runs on the host cores, with the CPU model and the
+                BLAS threads in use, and one-thread runs on the 64-atom cell
+                and a sample of the 512-atom cell;
+  conditioning  kappa_E and kappa_F of the workload (oracle/conditioning.json);
   neighbors_ms  the neighbour build on its own (warm, preallocated buffers,
                 its host synchronisation included; the first, cold build as
                 neighbors_first_ms), and with_neighbours: a build followed by
                 the call, per step.
+
+--mode suite times every workload (64, 512, 4096-atom diamond, rocksalt,
+perovskite, 32768-atom diamond at 128 channels) in ABBA order (each workload
+visited twice, the second pass in reverse), one JSON line per workload with
+per-call P50/P90 over both visits.
 """
 from __future__ import annotations
 
@@ -43,6 +59,13 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+# BLAS / OpenMP threads of the CPU baseline: the cores this process may run on,
+# fixed before NumPy is first imported (a count the environment already sets
+# is kept).
+HOST_CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(HOST_CORES))
 
 METRIC = "edges/s fwd+force bwd, fp32, 4096-atom diamond (E≈6.5e5); % of roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3
@@ -71,9 +94,9 @@ TAB_FLOP_PER_EDGE = 2 * (2 * 64 * 10) + 2048 + 2048 + 2048 + 2 * 64
 
 
 def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int, n_atoms: int = 1 << 30):
+    """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
     if variant == "tabulated":
         return "k_fold_table", "forward", TAB_FLOP_PER_EDGE * n_edges + FUSED_FLOP_PER_UNIT * n_units
-    """(kernel, phase whose events bracket exactly that launch, algorithmic flops per launch)."""
     if variant == "folded" and n_species == 1:
         flop = (FOLD_FWD_FLOP_PER_EDGE + BWD_FLOP_PER_EDGE["folded"]) * n_edges + FUSED_FLOP_PER_UNIT * n_units
         # up to 768 receivers the library gives each a workgroup (k_fold_split)
@@ -85,6 +108,8 @@ def dominant_kernel(variant: str, n_species: int, n_edges: int, n_units: int, n_
         return "k_fold_multi", "forward", flop
     flop = BWD_FLOP_PER_EDGE[variant] * n_edges + BWD_FLOP_PER_UNIT[variant] * n_units
     return ("k_backward" if variant == "direct" else "k_fold_backward"), "backward", flop
+
+
 WORKLOADS = {
     "D4096": "diamond 8x8x8 conventional cells, 4096 atoms, a=3.567 A, rc=6.0 A, 0.02 A noise, seed 0, C=64",
     "D512": "diamond 4x4x4 conventional cells, 512 atoms, rc=6.0 A, C=64",
@@ -93,9 +118,11 @@ WORKLOADS = {
     "PV": "cubic perovskite 10x10x10 cells, 5000 atoms, 3 species, a=3.95 A, rc=6.0 A, C=64",
     "D32k": "diamond 16x16x16 conventional cells, 32768 atoms, rc=6.0 A, C=128",
 }
+SUITE = ("D64", "D512", "D4096", "RS", "PV", "D32k")
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CONDITIONING_FILE = os.path.join(ROOT, "oracle", "conditioning.json")
 
 
 def sources_digest() -> str:
@@ -126,8 +153,44 @@ def recorded_traffic(kernel: str, config_name: str):
     return float(rec["bytes_per_launch"])
 
 
-def cpu_baseline(cfg, n_rows: int = 1 << 30):
-    """The oracle (as it stands) on the first n_rows receivers of the workload."""
+def conditioning(config_name: str):
+    """kappa_E, kappa_F and RMS(F) of the workload from the oracle's table
+    (oracle/conditioning_table.py), or None when it has no entry."""
+    try:
+        with open(CONDITIONING_FILE) as f:
+            rec = json.load(f).get(config_name)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    return {k: rec[k] for k in ("kappa_E", "kappa_F", "rms_F")}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    """Threads of the BLAS library NumPy loaded (what the oracle's products use)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # threadpoolctl missing or unable to introspect
+        return int(os.environ.get("OMP_NUM_THREADS", HOST_CORES))
+
+
+def oracle_sample(cfg, n_rows: int):
+    """Seconds of the oracle's forward (basis, network, harmonics, message) and
+    force backward over the first n_rows receivers of a workload, and their
+    edge count."""
     import numpy as np
 
     from oracle import model as M
@@ -150,11 +213,36 @@ def cpu_baseline(cfg, n_rows: int = 1 << 30):
     np.add.at(A, recv, msg)
     Abar = 2.0 * w[None, None, :] * A
     M.edge_backward(d, pairs, hj, Abar[recv], cfg.model)
-    dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return {"value": e1 / dt, "unit": "edges/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_rows} receivers of the workload ({e1} edges): float64 forward "
-                      f"(basis, network, harmonics, message) and force backward; {dt:.2f} s"}
+    return time.perf_counter() - t0, e1
+
+
+def cpu_baseline(cfg, n_rows: int = 1024, repeats: int = 3):
+    """The oracle (as it stands) on the first n_rows receivers of the workload:
+    the median of `repeats` runs with the BLAS threads set at start-up, and
+    one-thread runs on the 64-atom diamond and the first 128 receivers of the
+    512-atom diamond."""
+    import numpy as np
+
+    import eec_inputs as I
+
+    runs = [oracle_sample(cfg, n_rows) for _ in range(repeats)]
+    dt = float(np.median([r[0] for r in runs]))
+    e1 = runs[0][1]
+    one = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            for name, rows in (("D64", 64), ("D512", 128)):
+                t, e = oracle_sample(I.make_config(name), rows)
+                one[name] = {"value": e / t, "unit": "edges/s", "edges": e, "receivers": rows, "s": t}
+    except ImportError:
+        one = None
+    return {"value": e1 / dt, "unit": "edges/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {min(n_rows, cfg.n_atoms)} receivers of the workload ({e1} edges): float64 "
+                      f"forward (basis, network, harmonics, message) and force backward; median of "
+                      f"{repeats} runs, {dt:.2f} s each",
+            "runs_s": [r[0] for r in runs], "cpu_model": cpu_model(), "host_cores": HOST_CORES,
+            "one_thread": one}
 
 
 def copy_calibration(args, torch, dev) -> int:
@@ -326,12 +414,159 @@ def md_mode(args, B, torch, cfg, model, dev) -> int:
     return 0
 
 
+class Workload:
+    """One workload on the device: inputs, model, neighbour list and the
+    number of (receiver, sender species) units with at least one edge."""
+
+    def __init__(self, B, torch, name: str, dev):
+        import numpy as np
+
+        import eec_inputs as I
+
+        self.name = name
+        self.cfg = cfg = I.make_config(name)
+        self.pos = torch.as_tensor(cfg.pos).to(dev)
+        self.species = torch.as_tensor(cfg.species).to(dev)
+        self.model = B.Model.from_arrays(cfg.model, dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.g = B.build_neighbors(self.pos, cfg.box, cfg.model.cutoff, self.species, cfg.model.n_species)
+        torch.cuda.synchronize()
+        self.nb_first_ms = (time.perf_counter() - t0) * 1e3
+        self.E = self.g.n_edges
+        rp = self.g.row_ptr.cpu().numpy()
+        if cfg.model.n_species == 1:
+            self.n_units = int(np.count_nonzero(np.diff(rp)))
+        else:
+            col = self.g.col.cpu().numpy()
+            recv = np.repeat(np.arange(self.g.n_atoms), np.diff(rp))
+            self.n_units = len(np.unique(recv.astype(np.int64) * cfg.model.n_species + cfg.species[col]))
+        self.table = None
+
+    def radial_table(self, B):
+        if self.table is None:
+            self.table = B.RadialTable(self.model, 6)
+        return self.table
+
+    def energy_forces(self, B, variant: str, dev):
+        return B.EnergyForces(self.g, self.model, dev, atom_energy=True, variant=variant,
+                              table=self.radial_table(B) if variant == "tabulated" else None)
+
+    def dominant(self, variant: str):
+        c = self.cfg
+        return dominant_kernel(variant, c.model.n_species, self.E, self.n_units, c.n_atoms)
+
+
+def preload(torch, ef, w, min_ms: float) -> dict:
+    """Untimed calls until at least min_ms of wall time has passed (the clock
+    settles under sustained load), then a device synchronisation."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            ef(w.pos, w.cfg.box, w.species)
+        n += 8
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            break
+    return {"ms": (time.perf_counter() - t0) * 1e3, "calls": n}
+
+
+def timed(B, torch, w, ef, variant: str, steps: int, warmup: int) -> dict:
+    """Timed region: `steps` calls between two device synchronisations, with
+    hipEvents around the dominant kernel's launch only.  Then the same number
+    of calls with every phase recorded (phases_ms and the per-call device time
+    call_ms, first to last kernel of a call; not part of the timed figure)."""
+    import numpy as np
+
+    nph = len(B.PHASES)
+    _, dom_phase, _ = w.dominant(variant)
+    dp = B.PHASES.index(dom_phase)
+    steps = max(steps, 1)
+    ev = B.HipEvents(2 * nph * steps)
+    for _ in range(warmup):
+        ef(w.pos, w.cfg.box, w.species)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        handles = [None] * (2 * nph)
+        handles[2 * dp], handles[2 * dp + 1] = ev.handles[2 * k], ev.handles[2 * k + 1]
+        ef(w.pos, w.cfg.box, w.species, events=handles)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom = [ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(steps)]
+    for k in range(steps):
+        ef(w.pos, w.cfg.box, w.species, events=ev.handles[2 * nph * k: 2 * nph * (k + 1)])
+    torch.cuda.synchronize()
+    phase_ms = {}
+    for p, name in enumerate(B.PHASES):
+        phase_ms[name] = float(np.mean([ev.elapsed_ms(2 * nph * k + 2 * p, 2 * nph * k + 2 * p + 1)
+                                        for k in range(steps)]))
+    calls = [ev.elapsed_ms(2 * nph * k, 2 * nph * k + 2 * nph - 1) for k in range(steps)]
+    ev.close()
+    return {"ms_per_step": dt * 1e3 / steps, "phases_ms": phase_ms, "energy": float(ef.energy.cpu()[0]),
+            "dom_ms": float(np.mean(dom)), "dom_p50_ms": float(np.median(dom)), "call_samples": calls}
+
+
+def pct(x, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(x, np.float64), q))
+
+
+def roofline(w, variant: str, launch_ms: float) -> dict:
+    kernel, _, flop = w.dominant(variant)
+    achieved = flop / (launch_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+            "traffic": recorded_traffic(kernel, w.name), "flop_per_launch": flop, "launch_ms": launch_ms}
+
+
+def suite_mode(args, B, torch, dev) -> int:
+    """Every workload, ABBA order, the headline variant: per workload the
+    per-call device time (P50, P90) over both visits and the dominant kernel's
+    roofline fraction."""
+    import numpy as np
+
+    order = list(SUITE) + list(reversed(SUITE))
+    res = {n: {"calls": [], "ms": [], "dom": []} for n in SUITE}
+    loaded = {}
+    for name in order:
+        if name not in loaded:
+            w = Workload(B, torch, name, dev)
+            loaded[name] = (w, w.energy_forces(B, args.variant, dev))
+        w, ef = loaded[name]
+        pre = preload(torch, ef, w, args.preload_ms)
+        r = timed(B, torch, w, ef, args.variant, args.steps, args.warmup)
+        res[name]["calls"] += r["call_samples"]
+        res[name]["ms"].append(r["ms_per_step"])
+        res[name]["dom"].append(r["dom_ms"])
+        res[name]["preload"] = pre
+        res[name]["phases_ms"] = r["phases_ms"]
+        print(json.dumps({"mode": "suite_visit", "config": name, "ms_per_step": r["ms_per_step"],
+                          "dom_ms": r["dom_ms"]}), flush=True)
+    for name in SUITE:
+        w, _ = loaded[name]
+        rr = res[name]
+        ms = float(np.mean(rr["ms"]))
+        dom = float(np.mean(rr["dom"]))
+        print(json.dumps({"mode": "suite", "config": name, "workload": WORKLOADS[name], "variant": args.variant,
+                          "n_atoms": w.cfg.n_atoms, "n_edges": w.E, "ms_per_step": ms, "edges_per_s": w.E / (ms * 1e-3),
+                          "call_ms": {"p50": pct(rr["calls"], 50), "p90": pct(rr["calls"], 90),
+                                      "n": len(rr["calls"])},
+                          "phases_ms": rr["phases_ms"], "roofline": roofline(w, args.variant, dom),
+                          "conditioning": conditioning(name), "preload": rr["preload"]}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed calls first; the clock needs some tens of ms of load to settle")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed calls after the pre-load")
+    ap.add_argument("--preload-ms", type=float, default=1000.0,
+                    help="untimed calls of the headline variant for at least this much wall time before "
+                         "the warm-up (the clock needs sustained load to settle); reported as `preload`")
     ap.add_argument("--config", default="D4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-variant", action="store_true",
@@ -341,12 +576,13 @@ def main() -> int:
                          "last radial layer moved past the edge sum (eec_energy_forces_folded); "
                          "tabulated: s2 and ds2/dr from certified radial tables "
                          "(eec_energy_forces_tabulated, approximate, one to three species)")
-    ap.add_argument("--mode", default="energy_forces", choices=["energy_forces", "edge_message", "copy", "md"],
-                    help="energy_forces: the headline call; edge_message: the chunked streaming "
-                         "forward (radial rows + message pass), for profiling its kernels; copy: a "
-                         "plain 256 MiB device copy, the calibration of the HBM byte counters; md: an "
-                         "MD-like loop with a Verlet-skin neighbour list, rebuilt serially or on a "
-                         "side stream, against a rebuild before every call")
+    ap.add_argument("--mode", default="energy_forces",
+                    choices=["energy_forces", "suite", "edge_message", "copy", "md"],
+                    help="energy_forces: the headline call; suite: every workload in ABBA order; "
+                         "edge_message: the chunked streaming forward (radial rows + message pass), for "
+                         "profiling its kernels; copy: a plain 256 MiB device copy, the calibration of the "
+                         "HBM byte counters; md: an MD-like loop with a Verlet-skin neighbour list, rebuilt "
+                         "serially or on a side stream, against a rebuild before every call")
     ap.add_argument("--skin", type=float, default=0.2, help="Verlet skin of --mode md, A")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -363,91 +599,37 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.mode == "copy":
         return copy_calibration(args, torch, dev)
+    if args.mode == "suite":
+        return suite_mode(args, B, torch, dev)
     cfg = I.make_config(args.config)
     if args.mode == "md":
         return md_mode(args, B, torch, cfg, B.Model.from_arrays(cfg.model, dev), dev)
-    pos = torch.as_tensor(cfg.pos).to(dev)
-    species = torch.as_tensor(cfg.species).to(dev)
-    model = B.Model.from_arrays(cfg.model, dev)
 
-    # neighbour list (context; not in the timed step)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g = B.build_neighbors(pos, cfg.box, cfg.model.cutoff, species, cfg.model.n_species)
-    torch.cuda.synchronize()
-    nb_ms = (time.perf_counter() - t0) * 1e3
-    E = g.n_edges
-
+    w = Workload(B, torch, args.config, dev)
     if args.mode == "edge_message":
-        return message_mode(args, B, torch, cfg, g, pos, species, model, dev)
-    # units with at least one edge: (receiver, sender species) pairs present in the graph
-    rp = g.row_ptr.cpu().numpy()
-    if cfg.model.n_species == 1:
-        n_units = int(np.count_nonzero(np.diff(rp)))
-    else:
-        col = g.col.cpu().numpy()
-        recv = np.repeat(np.arange(g.n_atoms), np.diff(rp))
-        n_units = len(np.unique(recv.astype(np.int64) * cfg.model.n_species + cfg.species[col]))
-    nph = len(B.PHASES)
-
-    def timed(variant, steps, warmup):
-        """Timed region: `steps` calls, with hipEvents around the dominant
-        kernel's launch only; then the same number of calls with every phase
-        recorded (phases_ms, not part of the timed figure)."""
-        ef = B.EnergyForces(g, model, dev, atom_energy=True, variant=variant,
-                            table=table if variant == "tabulated" else None)
-        _, dom_phase, _ = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
-        dp = B.PHASES.index(dom_phase)
-        ev = B.HipEvents(2 * nph * max(steps, 1))
-        for _ in range(warmup):
-            ef(pos, cfg.box, species)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(steps):
-            handles = [None] * (2 * nph)
-            handles[2 * dp], handles[2 * dp + 1] = ev.handles[2 * k], ev.handles[2 * k + 1]
-            ef(pos, cfg.box, species, events=handles)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        dom_ms = float(np.mean([ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(steps)]))
-        for k in range(steps):
-            ef(pos, cfg.box, species, events=ev.handles[2 * nph * k: 2 * nph * (k + 1)])
-        torch.cuda.synchronize()
-        phase_ms = {}
-        for p, name in enumerate(B.PHASES):
-            phase_ms[name] = float(np.mean([ev.elapsed_ms(2 * nph * k + 2 * p, 2 * nph * k + 2 * p + 1)
-                                            for k in range(steps)]))
-        ev.close()
-        return dt * 1e3 / steps, phase_ms, float(ef.energy.cpu()[0]), dom_ms
-
-    table = None
-    if args.variant == "tabulated" or (cfg.model.n_species <= 3 and not args.no_other_variant):
-        table = B.RadialTable(model, 6)
-        cert = [float(x) for x in table.certificate.cpu()]
-    ms_per_step, phase_ms, energy, dom_ms = timed(args.variant, args.steps, args.warmup)
+        return message_mode(args, B, torch, cfg, w.g, w.pos, w.species, w.model, dev)
+    E = w.E
+    ef = w.energy_forces(B, args.variant, dev)
+    pre = preload(torch, ef, w, args.preload_ms)
+    head = timed(B, torch, w, ef, args.variant, args.steps, args.warmup)
     others = [v for v in ("folded", "direct", "tabulated") if v != args.variant
-              and (v != "tabulated" or table is not None)]
+              and (v != "tabulated" or cfg.model.n_species <= 3)]
     other_res = {}
     if not args.no_other_variant:
         for other in others:
-            other_res[other] = timed(other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
-
-    def roof(variant, launch_ms):
-        kernel, phase, flop = dominant_kernel(variant, cfg.model.n_species, E, n_units, cfg.n_atoms)
-        return kernel, flop, launch_ms, flop / (launch_ms * 1e-3) / 1e12
+            ef_o = w.energy_forces(B, other, dev)
+            other_res[other] = timed(B, torch, w, ef_o, other, max(args.steps // 2, 1), max(args.warmup // 2, 1))
 
     # the neighbour build timed on its own (warm, into preallocated buffers,
     # host synchronisation included), and build + call per step
-    nl = B.NeighborList(cfg.n_atoms, cfg.box, cfg.model.cutoff, E + 1024, dev, species, cfg.model.n_species)
-    ef_nb = B.EnergyForces(g, model, dev, atom_energy=True, variant=args.variant,
-                           table=table if args.variant == "tabulated" else None)
+    nl = B.NeighborList(cfg.n_atoms, cfg.box, cfg.model.cutoff, E + 1024, dev, w.species, cfg.model.n_species)
     for _ in range(5):
-        nl.build(pos)
+        nl.build(w.pos)
     nb_times = []
     for _ in range(20):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        nl.build(pos)
+        nl.build(w.pos)
         torch.cuda.synchronize()
         nb_times.append((time.perf_counter() - t0) * 1e3)
     nb_warm_ms = float(np.median(nb_times))
@@ -455,11 +637,12 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(n_with):
-        ef_nb(pos, cfg.box, species, graph=nl.build(pos))
+        ef(w.pos, cfg.box, w.species, graph=nl.build(w.pos))
     torch.cuda.synchronize()
     with_ms = (time.perf_counter() - t0) * 1e3 / n_with
 
-    kernel, flop, launch_ms, achieved = roof(args.variant, dom_ms)
+    ms_per_step = head["ms_per_step"]
+    calls = head["call_samples"]
     out = {
         "metric": METRIC,
         "value": E / (ms_per_step * 1e-3),
@@ -475,23 +658,26 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "n_atoms": cfg.n_atoms,
                    "n_edges": E, "channels": cfg.model.channels, "n_species": cfg.model.n_species},
-        "roofline": {"bound": "mfma", "kernel": kernel,
-                     "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": recorded_traffic(kernel, args.config),
-                     "flop_per_launch": flop, "launch_ms": launch_ms},
+        "roofline": roofline(w, args.variant, head["dom_ms"]),
         "variant": args.variant,
+        "preload": pre,
+        "call_ms": {"p50": pct(calls, 50), "p90": pct(calls, 90), "mean": float(np.mean(calls)), "n": len(calls),
+                    "kernel_p50": head["dom_p50_ms"]},
         "variants": {
-            other: {"ms_per_step": o_ms, "value": E / (o_ms * 1e-3), "phases_ms": o_phase, "energy": o_energy,
-                    "roofline_kernel": roof(other, o_dom)[0], "kernel_ms": o_dom,
-                    "roofline_frac": roof(other, o_dom)[3] / PEAK_FP32_MFMA_TFLOPS,
-                    **({"table_certificate": cert, "approximate": True} if other == "tabulated" else {})}
-            for other, (o_ms, o_phase, o_energy, o_dom) in other_res.items()},
-        "phases_ms": phase_ms,
+            other: {"ms_per_step": r["ms_per_step"], "value": E / (r["ms_per_step"] * 1e-3),
+                    "phases_ms": r["phases_ms"], "energy": r["energy"],
+                    "call_ms": {"p50": pct(r["call_samples"], 50), "p90": pct(r["call_samples"], 90)},
+                    "roofline_kernel": w.dominant(other)[0], "kernel_ms": r["dom_ms"],
+                    "roofline_frac": roofline(w, other, r["dom_ms"])["frac"],
+                    **({"table_certificate": [float(x) for x in w.table.certificate.cpu()], "approximate": True}
+                       if other == "tabulated" else {})}
+            for other, r in other_res.items()},
+        "phases_ms": head["phases_ms"],
         "neighbors_ms": nb_warm_ms,
-        "neighbors_first_ms": nb_ms,
+        "neighbors_first_ms": w.nb_first_ms,
         "with_neighbours": {"ms_per_step": with_ms, "value": E / (with_ms * 1e-3), "steps": n_with},
-        "energy": energy,
+        "energy": head["energy"],
+        "conditioning": conditioning(args.config),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -8,9 +8,12 @@
 //
 // Pipeline (one host synchronisation, after the row counts):
 //   bin atoms into cells of side >= rc  ->  exclusive scan of cell counts  ->
-//   place atoms  ->  count edges per row (one wave per receiver, lanes over the
-//   27 neighbouring (cell, image) candidates)  ->  scan  ->  [sync: E, flags]
-//   ->  fill each row with (j, n) keys  ->  rank-sort each row  ->  reverse index.
+//   place atoms, with their positions, in cell order  ->  one pass over the 27
+//   neighbouring (cell, image) candidates of every receiver (a wave each) that
+//   writes the row's (j, n) keys into the receiver's key slots and counts the
+//   row  ->  scan of the row counts  ->  [sync: E, flags]  ->  (only when a row
+//   outgrew its slots: a second pass writing every row's keys at its CSR
+//   offsets)  ->  sort each row  ->  reverse index.
 #include <math.h>
 
 #include <algorithm>
@@ -366,8 +369,7 @@ __device__ __forceinline__ int32_t key_at(const int32_t* __restrict__ col,
 __global__ void __launch_bounds__(256) k_nb_rev(int32_t n, const int32_t* __restrict__ rp,
                                                 const int32_t* __restrict__ col,
                                                 const int8_t* __restrict__ shift,
-                                                int32_t* __restrict__ rev,
-                                                uint32_t* __restrict__ flags) {
+                                                int32_t* __restrict__ rev) {
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
@@ -384,12 +386,11 @@ __global__ void __launch_bounds__(256) k_nb_rev(int32_t n, const int32_t* __rest
       if (col[mid] < i) lo = mid + 1; else hi = mid;
     }
     while (lo < end && col[lo] == i && key_at(col, shift, lo) < target) ++lo;
-    if (lo < end && key_at(col, shift, lo) == target) {
-      rev[e] = lo;
-    } else {
-      rev[e] = e;
-      atomicOr(flags, FLAG_GEOMETRY);
-    }
+    // The reverse edge always exists: d of (j, i, -n) is -d bit for bit and
+    // the binary64 cutoff test squares each component, so both directions get
+    // the same decision, and the candidate enumeration is symmetric.  The
+    // fallback only keeps rev in bounds.
+    rev[e] = (lo < end && key_at(col, shift, lo) == target) ? lo : e;
   }
 }
 
@@ -518,7 +519,9 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
   k_scan_excl<<<1, 1024, 0, s>>>(deg, n, rp_tmp, total);
   // The flags and the edge total come back through a 16-byte pinned host word
   // kept per host thread (a copy into pageable memory is staged, and cost as
-  // much as the kernels on small cells); allocated on the first build.
+  // much as the kernels on small cells); allocated on the thread's first build
+  // and kept until the process ends (freeing it at thread exit could run after
+  // the HIP runtime has shut down).
   struct Readback {
     uint32_t flags;
     uint32_t pad;
@@ -554,7 +557,7 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
     } else {
       k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, nullptr, slots, col, shift);
     }
-    k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev, flags);
+    k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev);
   }
   if (hipGetLastError() != hipSuccess) { *why = "kernel launch failed"; return EEC_ERR_HIP; }
   return EEC_OK;

@@ -138,7 +138,7 @@ typedef struct {
  *              second pass over the candidates)
  * Synchronises `stream` once (to read E and the validity flags, through a
  * 16-byte pinned host word that the library allocates on a thread's first
- * call and keeps); the CSR arrays are written after that, on `stream`, so
+ * call and keeps until the process ends); the CSR arrays are written after that, on `stream`, so
  * work on another stream that reads them must wait for `stream` (an event).  The out-of-box, species and
  * coincident-atom checks are made on the device before any CSR array is
  * written.  A list built with a cutoff larger than the model's (a Verlet skin)

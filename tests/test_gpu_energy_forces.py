@@ -4,6 +4,8 @@ Tolerances: energy within 1e-5 relative; forces max|dF| <= 1e-4 RMS(F);
 every output finite.  The message A is compared to 2e-5 of its largest
 magnitude (float32 sums of <= 158 products of O(1) terms)."""
 import dataclasses
+import json
+import os
 
 import numpy as np
 import pytest
@@ -16,6 +18,8 @@ from oracle import neighbors as N
 from oracle.sampled import sampled_energy_forces
 
 from gpu_util import device_inputs, graph_for, np_, rms, say
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 pytestmark = pytest.mark.gpu
 
@@ -97,10 +101,11 @@ def test_energy_forces_elementwise_wave_per_receiver(name, variant):
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("cutoff", [6.5, 7.5])
 def test_dense_rows(cutoff, variant):
-    # rows of 6 (rc 6.5: 190 edges) and 10 (rc 7.5: 292-296 edges) tiles of 32:
-    # the folded one-species kernel keeps the first six tiles of a row for its
-    # backward and recomputes the rest, so both branches run; the cell side is
-    # below 2 rc (several images of one atom)
+    # rows of 6 (rc 6.5: 190 edges) and 10 (rc 7.5: 292-296 edges) tiles of 32
+    # on 512 receivers: the folded call gives each pair of receivers a
+    # workgroup whose eight waves share the rows' tiles (no wave holds more
+    # than three, so every tile's backward reads its stash rows); the cell side
+    # is below 2 rc (several images of one atom)
     say(f"[energy_forces] dense D512 rc={cutoff} {variant}")
     base = I.make_config("D512")
     cfg = dataclasses.replace(base, model=dataclasses.replace(base.model, cutoff=cutoff))
@@ -115,6 +120,57 @@ def test_dense_rows(cutoff, variant):
     assert abs(float(out["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
     assert np.abs(out["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
     assert np.abs(out["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+
+
+def _with_cutoff(name, rc):
+    base = I.make_config(name)
+    return dataclasses.replace(base, model=dataclasses.replace(base.model, cutoff=rc))
+
+
+def _tiles_per_receiver(cfg, g):
+    """32-edge tiles of each receiver's (receiver, sender species) units."""
+    rp, col = np_(g.row_ptr).astype(np.int64), np_(g.col)
+    S = cfg.model.n_species
+    return np.array([sum((np.count_nonzero(cfg.species[col[rp[i]:rp[i + 1]]] == z) + 31) // 32 for z in range(S))
+                     for i in range(cfg.n_atoms)])
+
+
+_OVERFLOW_REF = {}
+
+
+@pytest.mark.parametrize("variant", VARIANTS + ["tabulated"])
+@pytest.mark.parametrize("name,rc", [("D1728", 7.5), ("RS3", 11.0), ("PV3", 8.0)])
+def test_stash_overflow(name, rc, variant):
+    # The folded and tabulated kernels that run a receiver in one wave keep the
+    # activations of its first six tiles for the backward and recompute any
+    # further tile.  One species with more than 768 receivers and rows of ten
+    # tiles (the wave-per-receiver kernel, k_fold_fused / k_fold_table); two
+    # species with nine tiles per receiver over its two sender species; three
+    # species where receivers have five to seven tiles (both sides of the
+    # limit in one call).
+    say(f"[stash overflow] {name} rc={rc} {variant}")
+    cfg = _with_cutoff(name, rc)
+    pos, species, model = device_inputs(cfg)
+    g = graph_for(cfg, pos, species)
+    tiles = _tiles_per_receiver(cfg, g)
+    assert tiles.max() > 6
+    if name == "PV3":
+        assert tiles.min() <= 6
+    if cfg.model.n_species == 1:
+        assert cfg.n_atoms > 768
+    table = B.RadialTable(model, 6) if variant == "tabulated" else None
+    got = {k: np_(v) for k, v in B.energy_forces(g, pos, cfg.box, species, model, virial=True, variant=variant,
+                                                   table=table).items()}
+    key = (name, rc)
+    if key not in _OVERFLOW_REF:
+        _OVERFLOW_REF[key] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
+    ref = _OVERFLOW_REF[key]
+    for k in ("energy", "atom_energy", "forces", "virial"):
+        assert np.all(np.isfinite(got[k])), k
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+    assert np.abs(got["virial"] - ref["virial"]).max() <= 1e-4 * np.abs(ref["virial"]).max()
 
 
 @pytest.mark.parametrize("name", ["D64", "PV3", "D512", "D64c128"])
@@ -156,41 +212,55 @@ def test_edge_message_full_size_sampled(name):
         assert np.abs(A[i] - A0).max() <= 2e-5 * np.abs(A0).max(), i
 
 
+_FULL_REF = {}
+
+
+def _full_oracle(name):
+    if name not in _FULL_REF:
+        cfg = I.make_config(name)
+        _FULL_REF[name] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+    return _FULL_REF[name]
+
+
 @pytest.mark.parametrize("variant", VARIANTS + ["tabulated"])
-@pytest.mark.parametrize("name,n_e,n_f", [("D4096", 256, 3), ("RS", 256, 6), ("PV", 256, 4), ("D32k", 96, 2)])
-def test_full_size_sampled(name, n_e, n_f, variant):
-    """Full-size cells in the benchmark's launch configuration; exact per-atom
-    energies and forces of sampled atoms from the oracle."""
+@pytest.mark.parametrize("name", ["D4096", "RS", "PV"])
+def test_full_size_every_atom(name, variant):
+    """Full-size cells in the benchmark's launch configuration (at 4,096 and
+    5,000 receivers the one-wave-per-receiver kernels loop over the grid, a
+    wave taking two or more receivers) against the full float64 oracle: the
+    energy, every atom's energy and every atom's force."""
     say(f"[full-size] {name} {variant}")
     cfg, pos, species, model, g, got = _run(name, variant=variant)
     for k in ("energy", "atom_energy", "forces"):
         assert np.all(np.isfinite(got[k])), k
+    ref = _full_oracle(name)
+    assert g.n_edges == ref["csr"].n_edges
+    assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
+    assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+
+
+@pytest.mark.parametrize("variant", VARIANTS + ["tabulated"])
+def test_full_size_sampled_d32k(variant):
+    """The 32,768-atom diamond at 128 channels in the benchmark's launch
+    configuration: exact per-atom energies of 128 atoms and forces of 12 from
+    the sampled oracle; the force scale is the full oracle's RMS(F)
+    (oracle/conditioning.json, written by oracle/conditioning_table.py)."""
+    say(f"[full-size] D32k {variant}")
+    cfg, pos, species, model, g, got = _run("D32k", variant=variant)
+    for k in ("energy", "atom_energy", "forces"):
+        assert np.all(np.isfinite(got[k])), k
+    with open(os.path.join(ROOT, "oracle", "conditioning.json")) as f:
+        cond = json.load(f)["D32k"]
     csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
+    assert g.n_edges == csr.n_edges == cond["n_edges"]
     rng = np.random.default_rng(123)
-    atoms = np.sort(rng.choice(cfg.n_atoms, n_e, replace=False))
-    fat = atoms[:n_f]
-    ref = sampled_energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, csr, atoms, forces_for=fat)
+    atoms = np.sort(rng.choice(cfg.n_atoms, 128, replace=False))
+    ref = sampled_energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, csr, atoms, forces_for=atoms[::11][:12])
     ei = got["atom_energy"][ref["atoms"]]
     assert np.abs(ei - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
-    # the force scale: RMS over all atoms of the GPU forces (an estimate of RMS(F))
-    Fs = rms(got["forces"])
-    assert np.abs(got["forces"][ref["force_atoms"]] - ref["F"]).max() <= 1e-4 * Fs
-    # total = float64 sum of the per-atom energies
-    tot = float(np.sum(got["atom_energy"].astype(np.float64)))
-    assert abs(float(got["energy"][0]) - tot) <= 1e-6 * np.abs(got["atom_energy"]).sum()
-    assert np.abs(got["forces"].astype(np.float64).sum(axis=0)).max() <= 1e-5 * np.abs(got["forces"]).sum()
-
-
-def test_full_energy_headline_cell():
-    """Total energy of the 4096-atom diamond against the full oracle forward."""
-    say("[full-size] D4096 total energy")
-    csr = None
-    for variant in VARIANTS:
-        cfg, *_, got = _run("D4096", variant=variant)
-        if csr is None:
-            csr = N.neighbors_celllist(cfg.pos, cfg.box, cfg.model.cutoff)
-            E0 = M.forward_edges(N.edge_vectors(cfg.pos, cfg.box, csr), csr, cfg.species, cfg.model)["E"]
-        assert abs(float(got["energy"][0]) - E0) <= 1e-5 * abs(E0), variant
+    assert np.abs(got["forces"][ref["force_atoms"]] - ref["F"]).max() <= 1e-4 * cond["rms_F"]
+    assert abs(float(got["energy"][0]) - cond["E"]) <= 1e-5 * abs(cond["E"])
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

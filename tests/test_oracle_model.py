@@ -290,3 +290,27 @@ def test_edge_direction_reading_only_flips_odd_degrees():
     sign = np.where(L % 2 == 1, -1.0, 1.0)
     assert np.allclose(f2["A"], f1["A"] * sign[None, :, None], atol=1e-12 * np.abs(f1["A"]).max())
     assert abs(f1["E"] - f2["E"]) <= 1e-12 * abs(f1["E"])
+
+
+# ------------------------------------------------------------- conditioning
+@pytest.mark.parametrize("r", [1.9, 4.4])
+def test_conditioning_closed_forms(r):
+    # kappa_E's numerator sum_i sum_c |w_c| sum_lm A^2 is the dimer closed form
+    # with |w|; kappa_F of a dimer is exactly sqrt 3: g_rev = -g_e, so |F_0| =
+    # 2|g| = the row's sum of |g_e| + |g_rev|, and RMS(F) over the six force
+    # components is |F_0| / sqrt 3
+    cfg = _dimer(r)
+    out = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+    dv = cfg.pos[1] - cfg.pos[0]
+    rr = math.sqrt((dv[0] * dv[0] + dv[1] * dv[1]) + dv[2] * dv[2])
+    kE, kF, rms = M.conditioning(out, cfg.model, out["csr"])
+    want = _dimer_closed_form(cfg, rr, absolute=True) / abs(_dimer_closed_form(cfg, rr))
+    assert want > 1.0
+    assert abs(kE - want) <= 1e-10 * want
+    assert abs(kF - math.sqrt(3.0)) <= 1e-12
+    assert abs(rms - float(np.linalg.norm(out["F"][0])) / math.sqrt(3.0)) <= 1e-12 * rms
+    # with every readout weight of one sign the energy cannot cancel: kappa_E = 1
+    pos_w = I.make_cluster(cfg.pos, cfg.box)
+    pos_w.model.w_read[:] = np.abs(pos_w.model.w_read)
+    out = M.energy_forces(pos_w.pos, pos_w.species, pos_w.box, pos_w.model)
+    assert abs(M.conditioning(out, pos_w.model, out["csr"])[0] - 1.0) <= 1e-12
