@@ -3,9 +3,15 @@
 The device-built tables against the oracle's: every coarse piece's level
 equal (or, where the two binary64 error estimates straddle the tolerance,
 both within 2 % of it), every kept coefficient within 3e-7 of its piece's
-largest coefficient (float32 storage), and the certificate of the same size as
-the one the oracle computes for its own float32-rounded table (both
-<= 3e-7).  The float32 table is
+largest coefficient (float32 storage).  The certificate the device reports is
+a claim about its own stored table, so it is checked against that table's
+error as the oracle's certificate routine measures it against the binary64
+chain (relative 1e-3: the same check points, a different summation order).
+It is also of the same size as the certificate of the oracle's own float32
+table (both <= 3e-7 at 32 or more coarse pieces); those two tables differ in
+the last bit of some coefficients, which moves the largest derivative error
+by up to about 20 % (measured 0.81-1.09), so that comparison is kept to a
+factor of two.  The float32 table is
 more accurate than the float32 network (the pages' certificate ratio < 1).
 The tabulated energy/force call against the float64 oracle of the exact
 network at the same bars as the other variants (energy 1e-5 relative, forces
@@ -59,7 +65,7 @@ def test_table_build_matches_oracle(name, K):
     # every word is written: the sub-piece slots past a piece's level are zeros
     used = np.arange(1 << TB.DMAX)[None, None, :] < (1 << levels)[:, :, None]
     assert np.all(coef[~used] == 0.0)
-    oracle_cert = [0.0, 0.0]
+    oracle_cert, measured = [0.0, 0.0], [0.0, 0.0]
     for p in range(P):
         fn = TB.pair_chain(m, p)
         lo, co = ref[p]
@@ -76,7 +82,10 @@ def test_table_build_matches_oracle(name, K):
             assert np.all(np.abs(a_g - a_o) <= 3e-7 * scale), (p, c)
         ev, ed = TB.certificate(lo, TB.power_form(co).astype(np.float32), fn, m.cutoff, K)
         oracle_cert = [max(oracle_cert[0], ev), max(oracle_cert[1], ed)]
-    say(f"[table_build] certificate {cert.tolist()} oracle {oracle_cert}")
+        dv, dd = TB.certificate(levels[p], coef[p], fn, m.cutoff, K)
+        measured = [max(measured[0], dv), max(measured[1], dd)]
+    say(f"[table_build] certificate {cert.tolist()} of the device table {measured} oracle table {oracle_cert}")
+    np.testing.assert_allclose(cert, measured, rtol=1e-3)
     for q in range(2):
         assert 0.5 <= cert[q] / oracle_cert[q] <= 2.0
     if K >= 5:
