@@ -373,7 +373,7 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, int nparts, const fl
 // thread a contiguous slice of atoms, then a tree.  E = sum_i E_i; with VIRIAL,
 // W = sum_i vpart_i.
 constexpr int TT = 256;   // k_totals
-constexpr int TS = 1024;  // k_scatter: 16 atoms per workgroup
+constexpr int TS = 512;   // k_scatter: 16 atoms per workgroup, 32 lanes each
 template <bool VIRIAL, int NTH>
 __device__ void block_totals(int32_t n, const float* __restrict__ ei, const double* __restrict__ vpart,
                              float* __restrict__ energy, float* __restrict__ virial) {
@@ -413,11 +413,16 @@ __global__ void __launch_bounds__(TT) k_totals(int32_t n, const float* __restric
 }
 
 // ------------------------------------------------------------ force scatter
-// One wave per atom: F_i = sum_{e in row i} (g_e - g_rev(e)); lanes take a fixed
-// stride of the row, then a fixed shuffle tree.  With VIRIAL, also the atom's
-// share of the virial -sum_e d_e g_e^T (in binary64).
+// Half a wave per atom: F_i = sum_{e in row i} (g_e - g_rev(e)); lane k of the
+// half takes edges k, k + 32, ... of the row (five per lane per pass: a
+// diamond row of 158 edges in one pass, every reverse index loaded before the
+// rows, every row and reverse row before the sums), then a fixed shuffle tree
+// over the 32 lanes.  With VIRIAL, also the atom's share of the virial
+// -sum_e d_e g_e^T (in binary64).
+constexpr int SLPA = 32;  // lanes per atom
+constexpr int SU = 5;     // edges per lane per pass
 template <bool VIRIAL>
-__device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t E,
+__device__ __forceinline__ void scatter_atom(bool live, int i, int k, int32_t n, int64_t E,
                                              const int32_t* __restrict__ rp, const int32_t* __restrict__ col,
                                              const int8_t* __restrict__ shift, const int32_t* __restrict__ rev,
                                              const double* __restrict__ pos, double Lx, double Ly, double Lz,
@@ -426,41 +431,30 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
   float fx = 0.f, fy = 0.f, fz = 0.f;
   double v[9];
 #pragma unroll
-  for (int k = 0; k < 9; ++k) v[k] = 0.0;
-  const int a = rp[i], b = rp[i + 1];
-  // Four 64-edge chunks per pass: every reverse index, then every gradient
-  // row, is loaded before the sums, which run edge by edge in the same order
-  // as one chunk at a time would.
-  constexpr int U = 4;
-  for (int e0 = a + lane; e0 < b; e0 += 64 * U) {
-    int er[U];
-    float ge[U][3], gr[U][3];
+  for (int q = 0; q < 9; ++q) v[q] = 0.0;
+  const int a = live ? rp[i] : 0, b = live ? rp[i + 1] : 0;
+  for (int e0 = a + k; e0 < b; e0 += SLPA * SU) {
+    int er[SU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) er[u] = e0 + 64 * u < b ? min(max(rev[e0 + 64 * u], 0), (int)E - 1) : 0;
+    for (int u = 0; u < SU; ++u) er[u] = e0 + SLPA * u < b ? min(max(rev[e0 + SLPA * u], 0), (int)E - 1) : 0;
+    float3 ge[SU], gr[SU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = min(e0 + 64 * u, b - 1);  // rows of 16 bytes: one load per edge
-      const float4 x = *reinterpret_cast<const float4*>(g + 4 * (size_t)e);
-      const float4 y = *reinterpret_cast<const float4*>(g + 4 * (size_t)er[u]);
-      ge[u][0] = x.x;
-      ge[u][1] = x.y;
-      ge[u][2] = x.z;
-      gr[u][0] = y.x;
-      gr[u][1] = y.y;
-      gr[u][2] = y.z;
+    for (int u = 0; u < SU; ++u) {
+      ge[u] = load_grad_row(g, min(e0 + SLPA * u, b - 1));
+      gr[u] = load_grad_row(g, er[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e0 + 64 * u;
+    for (int u = 0; u < SU; ++u) {
+      const int e = e0 + SLPA * u;
       if (e >= b) break;
-      fx += ge[u][0] - gr[u][0];
-      fy += ge[u][1] - gr[u][1];
-      fz += ge[u][2] - gr[u][2];
+      fx += ge[u].x - gr[u].x;
+      fy += ge[u].y - gr[u].y;
+      fz += ge[u].z - gr[u].z;
       if (VIRIAL) {
         const int j = min(max(col[e], 0), n - 1);
         double d[3];
         edge_vector(pos, i, j, shift + 3 * e, Lx, Ly, Lz, d);
-        const double gg[3] = {ge[u][0], ge[u][1], ge[u][2]};
+        const double gg[3] = {ge[u].x, ge[u].y, ge[u].z};
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
@@ -468,38 +462,38 @@ __device__ __forceinline__ void scatter_atom(int i, int lane, int32_t n, int64_t
       }
     }
   }
-  for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+  for (int off = SLPA / 2; off > 0; off >>= 1) {
     fx += __shfl_xor(fx, off);
     fy += __shfl_xor(fy, off);
     fz += __shfl_xor(fz, off);
     if (VIRIAL)
 #pragma unroll
-      for (int k = 0; k < 9; ++k) v[k] += __shfl_xor(v[k], off);
+      for (int q = 0; q < 9; ++q) v[q] += __shfl_xor(v[q], off);
   }
-  if (lane == 0) {
+  if (live && k == 0) {
     F[3 * i] = fx;
     F[3 * i + 1] = fy;
     F[3 * i + 2] = fz;
     if (VIRIAL)
 #pragma unroll
-      for (int k = 0; k < 9; ++k) vpart[9 * (size_t)i + k] = v[k];
+      for (int q = 0; q < 9; ++q) vpart[9 * (size_t)i + q] = v[q];
   }
 }
 
-// Forces of every atom, one wave per atom, 16 atoms per workgroup (the
-// gathered reverse-edge rows of consecutive atoms are adjacent rows of their
-// shared neighbours: a workgroup's waves reuse each other's cache lines in the
-// CU's L1).  The per-atom energies are
-// complete before this kernel starts, so when `energy` is given one extra
-// workgroup (the first, so that it runs beside the scatter rather than after
-// it) forms their total and the call needs no reduction launch for it; the
-// virial total needs the whole scatter and runs after it (k_totals).
-// Workgroups go to the eight XCDs in turn (workgroup b to XCD b mod 8), so
-// scatter workgroup v takes atom block (v mod 8) nv / 8 + v / 8 (nv, the
-// number of scatter workgroups, a multiple of 8): each XCD works through one
-// contiguous range of atoms, and the reverse-edge rows that neighbouring
-// atoms gather (adjacent rows of a shared neighbour, one cache line) are
-// fetched into its L2 once instead of once per XCD.
+// Forces of every atom, TS / SLPA = 16 atoms per workgroup (the gathered
+// reverse-edge rows of consecutive atoms are adjacent rows of their shared
+// neighbours: a workgroup's waves reuse each other's cache lines in the CU's
+// L1).  The per-atom energies are complete before this kernel starts, so when
+// `energy` is given one extra workgroup (the first, so that it runs beside the
+// scatter rather than after it) forms their total and the call needs no
+// reduction launch for it; the virial total needs the whole scatter and runs
+// after it (k_totals).  Workgroups go to the eight XCDs in turn (workgroup b
+// to XCD b mod 8), so scatter workgroup v takes atom block (v mod 8) nv / 8 +
+// v / 8 (nv, the number of scatter workgroups, a multiple of 8): each XCD
+// works through one contiguous range of atoms, and the reverse-edge rows that
+// neighbouring atoms gather (adjacent rows of a shared neighbour, one cache
+// line) are fetched into its L2 once instead of once per XCD.
 template <bool VIRIAL>
 __global__ void __launch_bounds__(TS) k_scatter(int32_t n, int64_t E, const int32_t* __restrict__ rp,
                                                 const int32_t* __restrict__ col,
@@ -509,6 +503,7 @@ __global__ void __launch_bounds__(TS) k_scatter(int32_t n, int64_t E, const int3
                                                 double Lz, const float* __restrict__ g,
                                                 float* __restrict__ F, double* __restrict__ vpart,
                                                 const float* __restrict__ ei, float* __restrict__ energy) {
+  constexpr int APB = TS / SLPA;
   const int first = energy != nullptr ? 1 : 0;
   const int nblk = gridDim.x - first;
   if (first && blockIdx.x == 0) {
@@ -517,9 +512,12 @@ __global__ void __launch_bounds__(TS) k_scatter(int32_t n, int64_t E, const int3
   }
   const int v = blockIdx.x - first;
   const int xv = (v & 7) * (nblk >> 3) + (v >> 3);
-  const int lane = threadIdx.x & 63;
-  for (int i = (int)((xv * blockDim.x + threadIdx.x) >> 6); i < n; i += (nblk * TS) >> 6)
-    scatter_atom<VIRIAL>(i, lane, n, E, rp, col, shift, rev, pos, Lx, Ly, Lz, g, F, vpart);
+  const int k = threadIdx.x % SLPA;
+  // the loop bound is uniform over the workgroup, so every lane reaches the shuffles
+  for (int base = xv * APB; base < n; base += nblk * APB) {
+    const int i = base + (int)(threadIdx.x / SLPA);
+    scatter_atom<VIRIAL>(i < n, min(i, n - 1), k, n, E, rp, col, shift, rev, pos, Lx, Ly, Lz, g, F, vpart);
+  }
 }
 
 // ------------------------------------------------------------ materialised basis
@@ -594,7 +592,7 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   p.off_A = o;     o += align256(4 * (size_t)p.S * N * NLM * p.C);  // S partial slabs
   p.off_R = o;     o += align256(4 * (size_t)p.chunk * p.NC);
   p.off_Y = o;     o += align256(4 * (size_t)p.chunk * NLM);
-  p.off_g = o;     o += align256(4 * 4 * (size_t)E);  // dE/dd per edge, padded to 16 bytes
+  p.off_g = o;     o += align256(4 * 3 * (size_t)E);  // dE/dd per edge, 12-byte rows
   p.off_ei = o;    o += align256(4 * (size_t)N);
   p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
   p.off_w3t = o;   o += align256(4 * (size_t)p.P * 64 * p.NC);
@@ -662,7 +660,7 @@ void launch_scatter(hipStream_t s, const ConvPlan& p, const eec_graph* g, const 
       k_totals<false><<<1, TT, 0, s>>>(0, ei, vpart, energy, virial);
     return;
   }
-  const int grid = (blocks_for(p.N, TS / 64) + 7) & ~7;  // a multiple of 8 (k_scatter's XCD mapping)
+  const int grid = (blocks_for(p.N, TS / SLPA) + 7) & ~7;  // a multiple of 8 (k_scatter's XCD mapping)
   if (virial) {
     k_scatter<true><<<grid, TS, 0, s>>>(p.N, p.E, g->row_ptr, g->col, g->shift, g->rev, pos, box.L[0], box.L[1],
                                          box.L[2], gin, forces, vpart, ei, nullptr);

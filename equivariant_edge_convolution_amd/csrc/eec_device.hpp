@@ -67,6 +67,17 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// dE/dd of an edge: one 12-byte row (three floats, no padding) of the
+// gradient array g [E][3], written by the backward kernels and gathered by
+// the force scatter.
+__device__ __forceinline__ void store_grad_row(float* __restrict__ g, int64_t e, float x, float y, float z) {
+  static_assert(sizeof(float3) == 12, "float3 rows of 12 bytes");
+  *reinterpret_cast<float3*>(g + 3 * e) = make_float3(x, y, z);
+}
+__device__ __forceinline__ float3 load_grad_row(const float* __restrict__ g, int64_t e) {
+  return *reinterpret_cast<const float3*>(g + 3 * e);
+}
+
 // XOR-swizzled row-major weight tile in LDS: element (row, col) of a matrix
 // with `ncols` columns (a multiple of 32).  Reads along a row (lanes over
 // columns) and down a column (lanes over rows) are both bank-conflict free.

@@ -478,9 +478,8 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
   rbar += __shfl_xor(rbar, 32);
   const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
   if (valid && h == 0) {
-    *reinterpret_cast<float4*>(gout + 4 * e) =
-        make_float4(rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
-                    rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r, 0.f);
+    store_grad_row(gout, e, rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
+                   rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r);
   }
   wave_sync_lds();
 }
@@ -1069,9 +1068,8 @@ __device__ __forceinline__ void bwd_tile_tab(const EdgeIn& in, const Recv& xi, c
   rbar += __shfl_xor(rbar, 32);
   const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
   if (valid && h == 0) {
-    *reinterpret_cast<float4*>(gout + 4 * e) =
-        make_float4(rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
-                    rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r, 0.f);
+    store_grad_row(gout, e, rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
+                   rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r);
   }
   wave_sync_lds();
 }

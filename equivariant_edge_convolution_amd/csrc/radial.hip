@@ -399,9 +399,8 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
 
     const float gu = G[0] * g.ux + G[1] * g.uy + G[2] * g.uz;
     if (valid && h == 0) {
-      *reinterpret_cast<float4*>(gout + 4 * e) =
-          make_float4(rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r, rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r,
-                      rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r, 0.f);
+      store_grad_row(gout, e, rbar * g.ux + (G[0] - gu * g.ux) * g.inv_r,
+                     rbar * g.uy + (G[1] - gu * g.uy) * g.inv_r, rbar * g.uz + (G[2] - gu * g.uz) * g.inv_r);
     }
   }
 }
