@@ -32,7 +32,8 @@ EEC_ERR_CAPACITY = 6
 SYMBOLS = (
     "eec_build_neighbors", "eec_neighbors_workspace_bytes", "eec_skin_check", "eec_radial_basis",
     "eec_radial_project", "eec_project_workspace_bytes", "eec_edge_message",
-    "eec_energy_forces", "eec_energy_forces_folded", "eec_energy_forces_timed", "eec_workspace_bytes",
+    "eec_energy_forces", "eec_energy_forces_folded", "eec_energy_forces_folded_noalloc",
+    "eec_energy_forces_timed", "eec_workspace_bytes",
     "eec_radial_table_floats", "eec_radial_table_levels", "eec_radial_table_build", "eec_energy_forces_tabulated", "eec_last_error",
 )
 PHASES = ("prepare", "forward", "readout", "backward", "scatter")
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.eec_energy_forces.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz]
     L.eec_energy_forces_folded.restype = ctypes.c_int
     L.eec_energy_forces_folded.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz]
+    L.eec_energy_forces_folded_noalloc.restype = ctypes.c_int
+    L.eec_energy_forces_folded_noalloc.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp]
     L.eec_energy_forces_timed.restype = ctypes.c_int
     L.eec_energy_forces_timed.argtypes = [vp, P(_Graph), vp, P(dbl), vp, P(_Model), vp, vp, vp, vp, vp, sz,
                                           i32, P(_Table), P(vp)]
@@ -382,6 +385,29 @@ def energy_forces(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, m
     out = dict(energy=ef.energy, atom_energy=ef.atom_energy, forces=ef.forces)
     if virial:
         out["virial"] = ef.virial
+    return out
+
+
+def energy_forces_folded_noalloc(graph: Graph, pos: torch.Tensor, box, species: torch.Tensor, model: Model,
+                                 virial: bool = False, out: dict | None = None):
+    """eec_energy_forces_folded_noalloc: the folded call with the library's
+    static device scratch instead of a workspace.  `out` (energy, atom_energy,
+    forces and optionally virial tensors, e.g. from an earlier call) is
+    written in place; otherwise the outputs are allocated here (by torch, on
+    the caller's side of the boundary)."""
+    dev = pos.device
+    n = graph.n_atoms
+    if out is None:
+        out = dict(energy=torch.empty(1, dtype=torch.float32, device=dev),
+                   atom_energy=torch.empty(n, dtype=torch.float32, device=dev),
+                   forces=torch.empty((n, 3), dtype=torch.float32, device=dev))
+        if virial:
+            out["virial"] = torch.empty((3, 3), dtype=torch.float32, device=dev)
+    g, m = graph.struct(), model.struct()
+    _check(lib().eec_energy_forces_folded_noalloc(_stream(dev), ctypes.byref(g), _ptr(pos), _box(box),
+                                                  _ptr(species), ctypes.byref(m), _ptr(out["energy"]),
+                                                  _ptr(out.get("atom_energy")), _ptr(out["forces"]),
+                                                  _ptr(out.get("virial"))), "energy_forces_folded_noalloc")
     return out
 
 

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "eec_device.hpp"
@@ -112,6 +113,40 @@ Span model_span(const float* p, const eec_model* m, int which) {
     case 4: return span(p, 4 * (size_t)m->n_species * C, "emb");
     default: return span(p, 4 * C, "w_read");
   }
+}
+
+// Scratch of eec_energy_forces_folded_noalloc: a file-scope device array (one
+// copy per GPU, held from the library's load until the process ends).  Host
+// code never passes the array's name to a kernel or a copy: the name is a
+// host-side stand-in, not a device address.  Its address on a device comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[EEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (which must be the
+// device of `stream`).
+eec_status scratch_on_current_device(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return fail(EEC_ERR_HIP, "no current HIP device (or a device index past 63)");
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return fail(EEC_ERR_HIP, "hipStreamGetDevice failed");
+    if (sdev != dev) return fail(EEC_ERR_SHAPE, "the stream belongs to a device other than the current one");
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(EEC_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EEC_OK;
 }
 
 }  // namespace
@@ -246,11 +281,14 @@ eec_status eec_edge_message(void* stream, const eec_graph* g, const double* pos,
   return launched("edge_message");
 }
 
+// noalloc: the folded variant (one to three species) in the layout of
+// fold_plan, with the static scratch as its workspace (the workspace
+// arguments are ignored).
 static eec_status energy_forces_impl(void* stream, const eec_graph* g, const double* pos,
                                      const double* box, const int32_t* species, const eec_model* m,
                                      float* energy, float* atom_energy, float* forces, float* virial,
                                      void* workspace, size_t workspace_bytes, int32_t variant,
-                                     const eec_radial_table* tab, void* const* events) {
+                                     const eec_radial_table* tab, void* const* events, bool noalloc = false) {
   if (variant != EEC_VARIANT_DIRECT && variant != EEC_VARIANT_FOLDED && variant != EEC_VARIANT_TABULATED)
     return fail(EEC_ERR_SHAPE, "unknown variant");
   TRY(check_graph(g));
@@ -267,8 +305,21 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     if (m->n_species > 3) return fail(EEC_ERR_SHAPE, "the tabulated variant takes one to three species");
     if (((uintptr_t)tab->coef & 7) != 0) return fail(EEC_ERR_SHAPE, "radial table must be 8-byte aligned");
   }
-  const ConvPlan p = conv_plan(g->n_atoms, g->n_edges, m);
-  TRY(check_ws(workspace, workspace_bytes, p.bytes));
+  if (noalloc) {
+    if (variant != EEC_VARIANT_FOLDED || m->n_species > 3)
+      return fail(EEC_ERR_SHAPE, "the no-allocation call is the folded variant for one to three species");
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
+  const ConvPlan p = noalloc ? fold_plan(g->n_atoms, g->n_edges, m) : conv_plan(g->n_atoms, g->n_edges, m);
+  if (noalloc) {
+    if (p.bytes > EEC_NOALLOC_SCRATCH_BYTES)
+      return fail(EEC_ERR_WORKSPACE, "the call needs " + std::to_string(p.bytes) +
+                                         " bytes of scratch; the static scratch holds " +
+                                         std::to_string((size_t)EEC_NOALLOC_SCRATCH_BYTES));
+  } else {
+    TRY(check_ws(workspace, workspace_bytes, p.bytes));
+  }
   const size_t N = (size_t)g->n_atoms;
   const Span tspan = tabulated ? span(tab->coef, 4 * table_floats(m->n_species, tab->log2_pieces), "radial table")
                                : span(nullptr, 0, "radial table");
@@ -286,6 +337,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     if (events != nullptr && events[k] != nullptr) hipEventRecord((hipEvent_t)events[k], s);
   };
   char* ws = (char*)workspace;
+  if (noalloc) TRY(scratch_on_current_device(s, &ws));
   float* A = (float*)(ws + p.off_A);
   float* ei = atom_energy ? atom_energy : (float*)(ws + p.off_ei);
   Box b{{box[0], box[1], box[2]}};
@@ -402,6 +454,13 @@ eec_status eec_energy_forces_folded(void* stream, const eec_graph* g, const doub
                                     size_t workspace_bytes) {
   return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, workspace,
                             workspace_bytes, EEC_VARIANT_FOLDED, nullptr, nullptr);
+}
+
+eec_status eec_energy_forces_folded_noalloc(void* stream, const eec_graph* g, const double* pos,
+                                            const double* box, const int32_t* species, const eec_model* m,
+                                            float* energy, float* atom_energy, float* forces, float* virial) {
+  return energy_forces_impl(stream, g, pos, box, species, m, energy, atom_energy, forces, virial, nullptr, 0,
+                            EEC_VARIANT_FOLDED, nullptr, nullptr, true);
 }
 
 eec_status eec_energy_forces_timed(void* stream, const eec_graph* g, const double* pos, const double* box,

@@ -601,6 +601,32 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   return p;
 }
 
+ConvPlan fold_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
+  ConvPlan p = conv_plan(n_atoms, n_edges, m);
+  // Only the regions of the folded one-kernel path (one to three species):
+  // the row-local species grouping and atom order (S > 1), dE/dd per edge,
+  // per-atom energies and virial partials, the Gram matrices or the
+  // transposed last layer, and the activation stash.  The other offsets are
+  // not carved (0) and no launch of that path reads them.
+  const int64_t N = std::max(n_atoms, 1), E = std::max<int64_t>(n_edges, 1);
+  p.off_recv = p.off_pair_start = p.off_blockcnt = p.off_A = p.off_R = p.off_Y = 0;
+  p.off_perm = p.off_seg = p.off_ord = p.off_zstart = 0;
+  size_t o = 0;
+  if (p.S > 1) {
+    p.off_perm = o;   o += align256(4 * (size_t)E);
+    p.off_seg = o;    o += align256(8 * (size_t)p.S * N);
+    p.off_ord = o;    o += align256(4 * (size_t)N);
+    p.off_zstart = o; o += 256;
+  }
+  p.off_g = o;     o += align256(4 * 3 * (size_t)E);
+  p.off_ei = o;    o += align256(4 * (size_t)N);
+  p.off_vpart = o; o += align256(8 * 9 * (size_t)N);
+  p.off_w3t = o;   o += align256(4 * (size_t)p.P * 64 * p.NC);
+  p.off_stash = o; o += align256(fold_stash_bytes(p));
+  p.bytes = o;
+  return p;
+}
+
 void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,
                     char* ws, float* zero_rows_of) {
   int32_t* recv = (int32_t*)(ws + p.off_recv);

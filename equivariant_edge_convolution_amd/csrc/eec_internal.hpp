@@ -56,6 +56,9 @@ struct ConvPlan {
   int64_t n_count_blocks;
 };
 ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
+// The smaller layout of the folded one-kernel path (one to three species):
+// only the regions that path reads and writes.
+ConvPlan fold_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m);
 
 // Graph preparation: receiver of each edge; pair-grouped edge order when S > 1.
 void launch_prepare(hipStream_t s, const ConvPlan& p, const eec_graph* g, const int32_t* species,

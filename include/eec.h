@@ -262,6 +262,29 @@ EEC_API eec_status eec_energy_forces_folded(void *stream, const eec_graph *g, co
                                     size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * eec_energy_forces_folded_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): eec_energy_forces_folded for one to three species with
+ * no workspace argument.  Its scratch is a fixed device array inside the
+ * library, EEC_NOALLOC_SCRATCH_BYTES (256 MiB) on every GPU the library is
+ * loaded on, held until the process ends; the call allocates nothing.
+ * Arguments and outputs as eec_energy_forces_folded (the caller still owns
+ * every input and output).  The current device must be the stream's device.
+ * The scratch holds about 214 MB of activation stash plus 12 bytes per edge
+ * and 76 bytes per atom (with S > 1 species 4 more bytes per edge and
+ * 4 + 8 S more per atom), so up to about 4.5 million edges: a larger call, or
+ * four species, is rejected (EEC_ERR_WORKSPACE, EEC_ERR_SHAPE) before any
+ * launch.  Every call on one GPU uses the same scratch, which keeps the last
+ * call's contents (nothing in it needs to start cleared): calls that overlap
+ * on one GPU (several streams or host threads) race and must be serialised
+ * by the caller.  Results are bit for bit those of eec_energy_forces_folded. */
+#define EEC_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+EEC_API eec_status eec_energy_forces_folded_noalloc(void *stream, const eec_graph *g, const double *pos,
+                                            const double *box /*[host][3]*/, const int32_t *species,
+                                            const eec_model *m, float *energy, float *atom_energy,
+                                            float *forces, float *virial);
+
+/* ------------------------------------------------------------------------
  * Radial tables -- the radial chain up to the folded last layer,
  * r -> s2(r) = silu(silu(b(r) W1) W2) (hidden width 64, per ordered species
  * pair), as piecewise polynomials of degree 10 on dyadic pieces of

@@ -144,3 +144,23 @@ def test_radial_table_host_side_errors():
     t = B._Table(6, 1 << 29, 1 << 30)
     args3 = (None, ctypes.byref(g), vp(1 << 16), box, vp(1 << 17), ctypes.byref(m3))
     assert B.STATUS[L.eec_energy_forces_tabulated(*args3, ctypes.byref(t), *outs)] == "EEC_ERR_SHAPE"
+
+
+def test_noalloc_host_side_rejections():
+    # the no-allocation call rejects four species and a call whose folded
+    # layout exceeds the static scratch, on the host, before any HIP call
+    L = B.lib()
+    box = (ctypes.c_double * 3)(60.0, 60.0, 60.0)
+    fake = dict(pos=ctypes.c_void_p(1 << 40), species=ctypes.c_void_p(1 << 41), energy=ctypes.c_void_p(1 << 42),
+                forces=ctypes.c_void_p(1 << 43))
+    args = lambda g, m: (None, ctypes.byref(g), fake["pos"], box, fake["species"], ctypes.byref(m), fake["energy"],
+                         None, fake["forces"], None)
+    g = B._Graph(32768, 5177344, 1 << 44, 1 << 45, 1 << 46, 1 << 47)  # 12 B/edge of dE/dd alone: 62 MB
+    st = L.eec_energy_forces_folded_noalloc(*args(g, _model_struct(n_species=4, fake_ptr=1 << 48)))
+    assert B.STATUS[st] == "EEC_ERR_SHAPE"
+    st = L.eec_energy_forces_folded_noalloc(*args(g, _model_struct(channels=128, fake_ptr=1 << 48)))
+    assert B.STATUS[st] == "EEC_ERR_WORKSPACE"
+    assert b"static scratch" in L.eec_last_error()
+    g = B._Graph(4096, 60_000_000, 1 << 44, 1 << 45, 1 << 46, 1 << 47)
+    st = L.eec_energy_forces_folded_noalloc(*args(g, _model_struct(fake_ptr=1 << 48)))
+    assert B.STATUS[st] == "EEC_ERR_WORKSPACE"
