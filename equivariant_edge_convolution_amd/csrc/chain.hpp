@@ -111,13 +111,51 @@ __device__ __forceinline__ void stage_rows(float* lds, int ld, const float* __re
   }
 }
 
-template <int C>
+// The same for a [ROWS][COLS] matrix staged by a workgroup of NT threads, in
+// rounds: each thread issues up to STAGE_WORDS 16-byte loads before it stores
+// any of them, so a round costs one memory latency (the loop above waits on
+// every load before its store); the cap keeps the words in flight within the
+// registers the kernels leave free.
+constexpr int STAGE_WORDS = 4;
+template <int ROWS, int COLS, int NT>
+__device__ __forceinline__ void stage_rows_all(float* lds, int ld, const float* __restrict__ g, float scale = 1.f) {
+  static_assert(COLS % 4 == 0, "rows of whole 16-byte words");
+  constexpr int N4 = ROWS * COLS / 4, PER = (N4 + NT - 1) / NT;
+  if ((reinterpret_cast<uintptr_t>(g) & 15) != 0) {
+    stage_rows(lds, ld, g, ROWS, COLS, scale);
+    return;
+  }
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += STAGE_WORDS) {
+    constexpr int R = PER < STAGE_WORDS ? PER : STAGE_WORDS;
+    float4 v[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = (int)threadIdx.x + (u0 + u) * NT;
+      if (u0 + u < PER && k < N4) v[u] = g4[k];
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = (int)threadIdx.x + (u0 + u) * NT;
+      if (u0 + u < PER && k < N4) {
+        float* d = lds + ((4 * k) / COLS) * ld + (4 * k) % COLS;
+        d[0] = v[u].x * scale;
+        d[1] = v[u].y * scale;
+        d[2] = v[u].z * scale;
+        d[3] = v[u].w * scale;
+      }
+    }
+  }
+}
+
+template <int C, int NT>
 __device__ __forceinline__ void stage_weights(float* lds, const float* __restrict__ W1, const float* __restrict__ W2,
-                              const float* __restrict__ W3, int p) {
+                              const float* __restrict__ W3, int p, float w1_scale = 1.f) {
   constexpr int NC = Lds<C>::NC;
-  stage_rows(lds + Lds<C>::W1, LDH, W1 + (size_t)p * NB * HID, NB, HID);
-  stage_rows(lds + Lds<C>::W2, LDH, W2 + (size_t)p * HID * HID, HID, HID);
-  stage_rows(lds + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC, HID, NC);
+  stage_rows_all<NB, HID, NT>(lds + Lds<C>::W1, LDH, W1 + (size_t)p * NB * HID, w1_scale);
+  stage_rows_all<HID, HID, NT>(lds + Lds<C>::W2, LDH, W2 + (size_t)p * HID * HID);
+  stage_rows_all<HID, NC, NT>(lds + Lds<C>::W3, Lds<C>::LD3, W3 + (size_t)p * HID * NC);
 }
 
 
@@ -316,12 +354,14 @@ struct Units {
   int S;
 };
 
-// W1 and W2 only (the reassociated kernels read the last layer from global memory).
+// W1 and W2 only (the reassociated kernels read the last layer from global
+// memory), by a workgroup of NT threads with every load issued first.
 constexpr int W12_FLOATS = NB * LDH + HID * LDH;
+template <int NT>
 __device__ __forceinline__ void stage_w12(float* lds, const float* __restrict__ W1,
                                           const float* __restrict__ W2, int p, float w1_scale = 1.f) {
-  stage_rows(lds, LDH, W1 + (size_t)p * NB * HID, NB, HID, w1_scale);
-  stage_rows(lds + NB * LDH, LDH, W2 + (size_t)p * HID * HID, HID, HID);
+  stage_rows_all<NB, HID, NT>(lds, LDH, W1 + (size_t)p * NB * HID, w1_scale);
+  stage_rows_all<HID, HID, NT>(lds + NB * LDH, LDH, W2 + (size_t)p * HID * HID);
 }
 
 // Position range [qa, qb) of unit (p, i) in the pair-grouped order; false when

@@ -571,11 +571,19 @@ ConvPlan conv_plan(int32_t n_atoms, int64_t n_edges, const eec_model* m) {
   p.P = p.S * p.S;
   p.E = n_edges;
   p.N = n_atoms;
-  // Chunk of streamed radial rows: 128 MiB of R, so the chunk the message pass
-  // reads back stays inside the 256 MB last-level cache.  Measured at 4,096
-  // atoms: halving it to 64 MiB costs 25 % (each launch of the radial kernel
-  // then gives every wave a single tile, and launch tails dominate).
-  const int64_t chunk_rows = (int64_t)(128 << 20) / (4 * p.NC);
+  // Chunk of streamed radial rows: at most 192 MiB of R, so the chunk the
+  // message pass reads back (with its harmonics) stays inside the 256 MB
+  // last-level cache, and a whole number of 32-edge tiles for each of the
+  // radial kernel's 2,048 waves (256 workgroups of 8), so no wave idles
+  // through a last round: 196,608 edges at 64 channels (three tiles a wave),
+  // 65,536 at 128 (one).  Measured at 4,096 atoms and 64 channels: 128 MiB
+  // chunks (two tiles a wave) run the radial kernel at 51 % of the matrix
+  // peak and the message pass at 4.9 TB/s, 192 MiB at 53 % and 5.6 TB/s;
+  // 256 MiB spills the cache (message pass 4.4 TB/s).  At 128 channels 1.5
+  // tiles a wave took the radial kernel from 59 % to 49 %.
+  constexpr int64_t TILE_ROUND = 256 * 8 * 32;
+  const int64_t fit_rows = (int64_t)(192 << 20) / (4 * p.NC);
+  const int64_t chunk_rows = std::max<int64_t>(TILE_ROUND, fit_rows / TILE_ROUND * TILE_ROUND);
   p.chunk = std::max<int64_t>(1, std::min<int64_t>(n_edges, chunk_rows));
   p.n_count_blocks = (n_edges + PB - 1) / PB;
   const int64_t N = std::max(n_atoms, 1), E = std::max<int64_t>(n_edges, 1);

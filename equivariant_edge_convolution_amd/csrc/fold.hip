@@ -193,13 +193,39 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
 constexpr int W3I_LD = 4 * 64 + 4;
 constexpr int W3I_FLOATS = HID * W3I_LD;
 
-// Stages W3[p] into the interleaved layout.
+// Stages W3[p] into the interleaved layout, by a workgroup of NT threads, in
+// rounds of STAGE_WORDS 16-byte words W3[k][l C + 4 q .. 4 q + 3] per thread
+// (all of a round's loads before its stores: one memory latency per round),
+// each spread over the four channels' words (degree l in slot l).
+template <int NT>
 __device__ __forceinline__ void stage_w3i(float* lds, const float* __restrict__ W3p) {
-  constexpr int C = 64;
-  for (int t = threadIdx.x; t < HID * C; t += blockDim.x) {
-    const int k = t / C, c = t % C;
-    const float* src = W3p + (size_t)k * 4 * C + c;
-    *reinterpret_cast<float4*>(lds + k * W3I_LD + 4 * c) = make_float4(src[0], src[C], src[2 * C], src[3 * C]);
+  constexpr int C = 64, N4 = HID * 4 * C / 4, PER = N4 / NT;
+  static_assert(N4 % NT == 0, "whole words per thread");
+  if ((reinterpret_cast<uintptr_t>(W3p) & 15) != 0) {
+    for (int t = threadIdx.x; t < HID * C; t += blockDim.x) {
+      const int k = t / C, c = t % C;
+      const float* src = W3p + (size_t)k * 4 * C + c;
+      *reinterpret_cast<float4*>(lds + k * W3I_LD + 4 * c) = make_float4(src[0], src[C], src[2 * C], src[3 * C]);
+    }
+    return;
+  }
+  const float4* g4 = reinterpret_cast<const float4*>(W3p);
+  static_assert(PER % STAGE_WORDS == 0, "whole rounds");
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += STAGE_WORDS) {
+    float4 v[STAGE_WORDS];
+#pragma unroll
+    for (int u = 0; u < STAGE_WORDS; ++u) v[u] = g4[threadIdx.x + (u0 + u) * NT];
+#pragma unroll
+    for (int u = 0; u < STAGE_WORDS; ++u) {
+      const int w = threadIdx.x + (u0 + u) * NT;  // word w: row k = w / 64, degree l = (w / 16) % 4, channels 4 (w % 16) ..
+      const int k = w >> 6, l = (w >> 4) & 3, c = 4 * (w & 15);
+      float* d = lds + k * W3I_LD + 4 * c + l;
+      d[0] = v[u].x;
+      d[4] = v[u].y;
+      d[8] = v[u].z;
+      d[12] = v[u].w;
+    }
   }
 }
 
@@ -269,7 +295,7 @@ k_fold_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* _
     const int p = b / nbp;
     if (p != loaded) {
       __syncthreads();
-      stage_w12(w12, W1, W2, p);
+      stage_w12<64 * W>(w12, W1, W2, p);
       __syncthreads();
       loaded = p;
     }
@@ -503,7 +529,7 @@ k_fold_backward(EdgeIn in, Units un, const float* __restrict__ W1, const float* 
     const int p = b / nbp;
     if (p != loaded) {
       __syncthreads();
-      stage_w12(w12, W1, W2, p);
+      stage_w12<64 * W>(w12, W1, W2, p);
       __syncthreads();
       loaded = p;
     }
@@ -691,7 +717,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   float* gs = wl + W12_FLOATS;
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  stage_w12(wl, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
+  stage_w12<64 * W>(wl, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
   stage_gram(gs, G);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
@@ -755,7 +781,7 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   const float* w1s = w12;
   const float* w2s = w12 + NB * LDH;
   const int N = un.n_atoms;
-  stage_w12(w12, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
+  stage_w12<64 * W>(w12, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
   __syncthreads();
   float* zw = stash + (size_t)(blockIdx.x * W + wave) * STASH_TILES * 32 * ZROW;
   // T block b register r, lane l: hidden 16 b + 4 (l / 16) + r, harmonic l % 16
@@ -1220,12 +1246,12 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
     if ((TAB && !W3L) || p == loaded) return;  // nothing to stage
     __syncthreads();
     if (TAB)
-      stage_w3i(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
+      stage_w3i<64 * W>(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
     else if (W3L) {
-      stage_w12(wl, W1, W2, p, KEXP);
-      stage_w3i(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
+      stage_w12<64 * W>(wl, W1, W2, p, KEXP);
+      stage_w3i<64 * W>(wl + MultiLds<C, W3L>::W3I, W3 + (size_t)p * HID * NC);
     } else
-      stage_w12(wl, W1, W2, p, KEXP);
+      stage_w12<64 * W>(wl, W1, W2, p, KEXP);
     __syncthreads();
     loaded = p;
   };

@@ -40,6 +40,7 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
          const float* __restrict__ basis_in, int64_t row_base, float* __restrict__ R_out,
          float* __restrict__ Y_out) {
   constexpr int NC = Lds<C>::NC;
+  constexpr bool SCALED = !BASIS_IN;
   __shared__ float lds[Lds<C>::FLOATS];
   __shared__ SchedState st;
   sched_init<W>(sc, st);
@@ -55,7 +56,7 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
     while (p + 1 < sc.P && st.bstart[p + 1] <= b) ++p;
     if (p != loaded) {
       __syncthreads();
-      stage_weights<C>(lds, W1, W2, W3, p);
+      stage_weights<C, 64 * W>(lds, W1, W2, W3, p, SCALED ? KEXP : 1.f);  // the scaled chain stages KEXP W1
       __syncthreads();
       loaded = p;
     }
@@ -72,7 +73,7 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
 #pragma unroll
       for (int k = 0; k < 16; ++k) bas[k] = basis_in[e * NB + 16 * h + k];
     } else {
-      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+      basis16f<false>(basis_seed(g.r, in.inv_rc, g.inv_r, h), in.inv_rc_f, h, bas, nullptr);
     }
     if (Y_out != nullptr && valid) {
       float Y[16];
@@ -83,33 +84,44 @@ k_radial(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restr
     }
     f32x16 z[2], a[2];
     layer1(w1s, bas, s, h, z);
-    silu_tiles(z, a);
+    silu_tiles_t<SCALED>(z, a);
     layer2(w2s, a, s, h, z);
-    silu_tiles(z, a);  // a = s2 (edges on N; as the A operand: edge = s)
+    silu_tiles_t<SCALED>(z, a);  // a = s2 (edges on N; as the A operand: edge = s), times KEXP when SCALED
 
     // output row of the edge held by accumulator register r (edge slot fperm(r) + 4h)
     const int my_row = valid ? (int)(e - row_base) : -1;
     int orow[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) orow[r] = __shfl(my_row, fperm(r) + 4 * h);
+    const bool full = __all(valid);
+    constexpr int HPL = C / 32;
+    float hcv[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j)
+      hcv[j] = (emb ? emb[(size_t)(p % n_species) * C + 32 * j + s] : 1.f) * (SCALED ? 1.f / KEXP : 1.f);
 
     // R = s2 W3 with edges on M: D[edge][feature], lane = feature 32 t + s.
     constexpr int LD3 = Lds<C>::LD3;
     const float* w3 = w3s + 4 * h * LD3 + s;  // W3[hid_k0(ks) + 4 h][32 t + s]
-    const float* hrow = emb ? emb + (size_t)(p % n_species) * C : nullptr;
 #pragma unroll 1
     for (int t = 0; t < NC / 32; ++t, w3 += 32) {
       f32x16 acc = zero16();
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks) acc = mfma32(a[ks >> 4][ks & 15], w3[hid_k0(ks) * LD3], acc);
-      if (hrow) {
-        const float hc = hrow[(32 * t + s) % C];
+      pipeline_lds_mfma<32, 1, 6>();
+      float hc = hcv[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] *= hc;
+      for (int j = 1; j < HPL; ++j) hc = (t % HPL) == j ? hcv[j] : hc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] *= hc;
+      if (full) {  // no padding slot in the tile: stores without per-row predicates
+#pragma unroll
+        for (int r = 0; r < 16; ++r) R_out[(size_t)orow[r] * NC + 32 * t + s] = acc[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (orow[r] >= 0) R_out[(size_t)orow[r] * NC + 32 * t + s] = acc[r];
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (orow[r] >= 0) R_out[(size_t)orow[r] * NC + 32 * t + s] = acc[r];
     }
   }
 }
@@ -146,7 +158,7 @@ k_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __rest
     const int p = b / nbp;
     if (p != loaded) {
       __syncthreads();
-      stage_weights<C>(lds, W1, W2, W3, p);
+      stage_weights<C, 64 * W>(lds, W1, W2, W3, p);
       __syncthreads();
       loaded = p;
     }
@@ -177,7 +189,7 @@ k_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __rest
       f32x16 z[2], a[2];
       {
         float bas[16];
-        basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+        basis16f<false>(basis_seed(g.r, in.inv_rc, g.inv_r, h), in.inv_rc_f, h, bas, nullptr);
         layer1(w1s, bas, s, h, z);
       }
       silu_tiles(z, a);
@@ -256,7 +268,7 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     while (p + 1 < sc.P && st.bstart[p + 1] <= b) ++p;
     if (p != loaded) {
       __syncthreads();
-      stage_weights<C>(lds, W1, W2, W3, p);
+      stage_weights<C, 64 * W>(lds, W1, W2, W3, p);
       __syncthreads();
       loaded = p;
     }
@@ -276,7 +288,7 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     f32x16 z[2], a[2];
     {
       float bas[16];
-      basis16<false>(g.r, in.rc, 16 * h + 1, bas, nullptr);
+      basis16f<false>(basis_seed(g.r, in.inv_rc, g.inv_r, h), in.inv_rc_f, h, bas, nullptr);
       layer1(w1s, bas, s, h, z);
     }
     silu_tiles(z, a);
@@ -361,7 +373,7 @@ k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __res
     // recompute the basis (with its r-derivative), z1 and z2: nothing of the
     // forward stays live through the loop above
     float bas[16], dbas[16];
-    basis16<true>(g.r, in.rc, 16 * h + 1, bas, dbas);
+    basis16f<true>(basis_seed(g.r, in.inv_rc, g.inv_r, h), in.inv_rc_f, h, bas, dbas);
     f32x16 z1[2], s1[2];
     layer1(w1s, bas, s, h, z1);
     silu_tiles(z1, s1);
