@@ -58,10 +58,13 @@ def test_energy_forces_elementwise(name, variant):
 @pytest.mark.parametrize("n_atoms", [300, 513])
 def test_split_kernel_ragged_receiver_pairs(n_atoms, variant):
     # a random subset of a perturbed diamond cell (so no two atoms closer than
-    # the crystal's bond), one species: between 256 and 768 atoms the folded
-    # call runs one workgroup per two receivers (i, i + 256); 300 and 513 leave
-    # most workgroups with one receiver of the pair missing, and 513 a third
-    # receiver in a second pass
+    # the crystal's bond), one species, up to 768 atoms, where both calls give
+    # each receiver a workgroup of eight waves sharing its tiles.  The folded
+    # kernel takes two receivers (i, i + 256) per workgroup pass: 300 and 513
+    # leave most workgroups with one receiver of the pair missing, and 513 a
+    # third receiver in a second pass.  The tabulated kernel takes one
+    # receiver per pass (i, i + 256, i + 512 in turn): 300 and 513 leave the
+    # workgroups with one, two or three passes.
     say(f"[energy_forces] split pairs, {n_atoms} atoms, {variant}")
     base = I.make_config("D512" if n_atoms < 512 else "D1728")  # rows of about 3 and 2 tiles
     keep = np.sort(np.random.default_rng(n_atoms).choice(base.n_atoms, n_atoms, replace=False))
