@@ -274,10 +274,11 @@ __global__ void __launch_bounds__(256) k_nb_fill(int32_t n, Grid gr, const doubl
 // One 64-thread workgroup per row: rank-sort the row's distinct keys and
 // write the sorted senders and image shifts.
 // With `slots`, row i's keys are read from slots + i * NB_SLOT_CAP (every row
-// then has at most NB_SLOT_CAP keys), else from keys + rp[i].
+// then has at most NB_SLOT_CAP keys) and written back there sorted, for the
+// reverse search; else they are read from keys + rp[i].
 __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __restrict__ rp,
                                                 const int32_t* __restrict__ keys_csr,
-                                                const int32_t* __restrict__ slots,
+                                                int32_t* __restrict__ slots,
                                                 int32_t* __restrict__ col, int8_t* __restrict__ shift) {
   __shared__ int32_t sk[SORT_LDS];
   const int i = blockIdx.x;
@@ -326,6 +327,12 @@ __global__ void __launch_bounds__(64) k_nb_sort(int32_t n, const int32_t* __rest
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * lane + r < deg) emit(4 * lane + r, v[r]);
+    if (slots != nullptr) {  // every lane's keys were read before the sort: no other lane reads these
+      int32_t* out = slots + (int64_t)i * NB_SLOT_CAP;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * lane + r < deg) out[4 * lane + r] = v[r];
+    }
   } else if (deg <= SORT_LDS) {
     // bitonic sort of the keys padded to a power of two (the pads sort last)
     int np2 = 64;
@@ -391,6 +398,61 @@ __global__ void __launch_bounds__(256) k_nb_rev(int32_t n, const int32_t* __rest
     // the same decision, and the candidate enumeration is symmetric.  The
     // fallback only keeps rev in bounds.
     rev[e] = (lo < end && key_at(col, shift, lo) == target) ? lo : e;
+  }
+}
+
+// The same from the sorted keys every row left in its slots (rows of at most
+// NB_SLOT_CAP = 256 edges): rev(e) = rp[j] + the position of key (i, -n) in
+// row j, by a lower-bound search of row j's sorted keys (one load per probe).
+// A lane's four edges (256 keys / 64 lanes) are searched together, so their
+// probes are in flight at once.
+__global__ void __launch_bounds__(256) k_nb_rev_slots(int32_t n, const int32_t* __restrict__ rp,
+                                                      const int32_t* __restrict__ slots,
+                                                      int32_t* __restrict__ rev) {
+  constexpr int U = NB_SLOT_CAP / 64;
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const int a = rp[i], deg = rp[i + 1] - a;
+  const int32_t* own = slots + (int64_t)i * NB_SLOT_CAP;
+  int32_t target[U];
+  int base[U], len[U], start[U];
+  const int32_t* rowj[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = lane + 64 * u;
+    const int32_t key = k < deg ? own[k] : 0;
+    const int j = min(max(key / 27, 0), n - 1);
+    target[u] = i * 27 + (26 - key % 27);
+    rowj[u] = slots + (int64_t)j * NB_SLOT_CAP;
+    start[u] = k < deg ? rp[j] : 0;
+    len[u] = k < deg ? rp[j + 1] - start[u] : 0;
+    base[u] = 0;
+  }
+  // lower bound of target in rowj[0 .. len): at most 9 halvings for 256 keys
+  for (int it = 0; it < 9; ++it) {
+    int32_t probe[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) probe[u] = len[u] > 0 ? rowj[u][base[u] + (len[u] >> 1)] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (len[u] <= 0) continue;
+      const int half = len[u] >> 1;
+      if (probe[u] < target[u]) {
+        base[u] += half + 1;
+        len[u] -= half + 1;
+      } else {
+        len[u] = half;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = lane + 64 * u;
+    if (k >= deg) continue;
+    const int cnt = rp[min(max(own[k] / 27, 0), n - 1) + 1] - start[u];
+    // the reverse edge always exists (see k_nb_rev); the fallback keeps rev in bounds
+    rev[a + k] = (base[u] < cnt && rowj[u][base[u]] == target[u]) ? start[u] + base[u] : a + k;
   }
 }
 
@@ -554,10 +616,11 @@ eec_status nb_build(hipStream_t s, const NbPlan& p, int32_t n, const double* pos
       k_nb_fill<false><<<blocks_for(n, 4), 256, 0, s>>>(n, gr, pos, cell_of, cell_start, cell_atoms, cell_pos,
                                                          row_ptr, rev /* keys staged here */, nullptr, nullptr);
       k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, rev, nullptr, col, shift);
+      k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev);
     } else {
       k_nb_sort<<<n, 64, 0, s>>>(n, row_ptr, nullptr, slots, col, shift);
+      k_nb_rev_slots<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, slots, rev);
     }
-    k_nb_rev<<<blocks_for(n, 4), 256, 0, s>>>(n, row_ptr, col, shift, rev);
   }
   if (hipGetLastError() != hipSuccess) { *why = "kernel launch failed"; return EEC_ERR_HIP; }
   return EEC_OK;
