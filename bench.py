@@ -125,16 +125,26 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CONDITIONING_FILE = os.path.join(ROOT, "oracle", "conditioning.json")
 
 
+def code_text(text: str) -> str:
+    """The code of a C++ source without its comments and blank space: what
+    the counters depend on (a comment edit leaves a traffic record valid)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (" ".join(line.split("//", 1)[0].split()) for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def sources_digest() -> str:
-    """SHA-256 over the kernel sources (csrc/*.hip, csrc/*.hpp, by name)."""
+    """SHA-256 over the code of the kernel sources (csrc/*.hip, csrc/*.hpp,
+    by name; comments and blank space excluded)."""
     import hashlib
     src = os.path.join(ROOT, "equivariant_edge_convolution_amd", "csrc")
     h = hashlib.sha256()
     for fn in sorted(os.listdir(src)):
         if fn.endswith((".hip", ".hpp")):
             h.update(fn.encode())
-            with open(os.path.join(src, fn), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(src, fn), encoding="utf-8") as f:
+                h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

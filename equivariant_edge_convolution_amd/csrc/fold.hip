@@ -61,10 +61,11 @@ struct WaveLds {
 //   [128, 136) u_x, u_y, u_z, 1/r, and the basis seed: x = r / rc as a float32
 //              head and tail, sin pi x, cos pi x
 // A unit's first STASH_TILES tiles are kept; further tiles (rows denser than
-// STASH_TILES * 32 edges) recompute.  The live rows of all waves (about 85 MB
-// for a 4096-atom diamond) stay in the last-level cache between the forward
-// and the backward of a unit, where re-reading them is cheaper than the two
-// layers it saves.
+// STASH_TILES * 32 edges) recompute.  The live rows of all waves (about 176
+// MB for a 4096-atom diamond: 2,048 waves, 158 edges each, 544 bytes an edge)
+// are read back mostly from the caches between the forward and the backward
+// of a unit (marking those reads non-temporal made the kernel 13 % slower),
+// which is cheaper than recomputing the basis and the two layers.
 constexpr int ZROW = 2 * HID + 8;
 constexpr int STASH_TILES = 6;
 

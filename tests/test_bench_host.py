@@ -47,3 +47,11 @@ def test_recorded_traffic_is_dropped_when_the_sources_change(tmp_path, monkeypat
     p.write_text(json.dumps(rec))
     assert bench.recorded_traffic("k_fold_fused", "D4096") == 1.0
     assert bench.recorded_traffic("k_fold_fused", "D512") is None
+
+
+def test_code_text_drops_comments_and_keeps_code():
+    a = "int f(int x) {  // doubles x\n  return 2 * x; /* not 3 */\n}\n"
+    b = "// a header line\nint f(int x) {\n\n    return 2 * x;\n}   // end\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(a.replace("2 * x", "3 * x"))
+    assert bench.code_text('p = "../../include/eec.h";') == 'p = "../../include/eec.h";'
