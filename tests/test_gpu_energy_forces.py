@@ -221,7 +221,7 @@ _FULL_REF = {}
 def _full_oracle(name):
     if name not in _FULL_REF:
         cfg = I.make_config(name)
-        _FULL_REF[name] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model)
+        _FULL_REF[name] = M.energy_forces(cfg.pos, cfg.species, cfg.box, cfg.model, want_virial=True)
     return _FULL_REF[name]
 
 
@@ -231,7 +231,9 @@ def test_full_size_every_atom(name, variant):
     """Full-size cells in the benchmark's launch configuration (at 4,096 and
     5,000 receivers the one-wave-per-receiver kernels loop over the grid, a
     wave taking two or more receivers) against the full float64 oracle: the
-    energy, every atom's energy and every atom's force."""
+    energy, every atom's energy and every atom's force; then the same call
+    with the virial (its own force pass and totals): the same forces bit for
+    bit, and the virial within 1e-4 of the oracle's largest component."""
     say(f"[full-size] {name} {variant}")
     cfg, pos, species, model, g, got = _run(name, variant=variant)
     for k in ("energy", "atom_energy", "forces"):
@@ -241,6 +243,11 @@ def test_full_size_every_atom(name, variant):
     assert abs(float(got["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
     assert np.abs(got["atom_energy"] - ref["Ei"]).max() <= 1e-5 * np.abs(ref["Ei"]).max()
     assert np.abs(got["forces"] - ref["F"]).max() <= 1e-4 * rms(ref["F"])
+    *_, gv = _run(name, virial=True, variant=variant)
+    np.testing.assert_array_equal(gv["forces"], got["forces"])
+    assert abs(float(gv["energy"][0]) - ref["E"]) <= 1e-5 * abs(ref["E"])
+    W0 = ref["virial"]
+    assert np.abs(gv["virial"] - W0).max() <= 1e-4 * np.abs(W0).max()
 
 
 @pytest.mark.parametrize("variant", VARIANTS + ["tabulated"])
