@@ -105,7 +105,10 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
   const BasisSeed sd = basis_seed(g.r, in.inv_rc, g.inv_r, h);
-  if (zs != nullptr && valid && h == 0) {
+  // Stash rows are written for all 32 slots, padding slots too (they hold the
+  // padding edge; the tile's 32 rows exist and slots past the unit's end are
+  // never read back), so no lane-dependent branch splits the stores.
+  if (zs != nullptr && h == 0) {
     float* row = zs + s * ZROW + 2 * HID;
     *reinterpret_cast<float4*>(row) = make_float4(g.ux, g.uy, g.uz, g.inv_r);
     *reinterpret_cast<float4*>(row + 4) = make_float4(sd.x, sd.xl, sd.s1, sd.c1);
@@ -119,7 +122,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
   if (zs != nullptr) {
     f32x16 d[2];
     silu_and_deriv_t<K>(z, a, d);  // s1 and silu'(z1), edges on N: hidden hid_k0(ks) + 4h
-    if (valid) {
+    {
       float* row = zs + s * ZROW + 4 * h;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -148,12 +151,9 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
     // z2 rows: register r of tile m is edge slot fperm(r) + 4h, hidden 32 m + s
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int k = fperm(r) + 4 * h;
-      if (q0 + k < qb) {
-        float* row = zs + k * ZROW + HID + s;
-        row[0] = z[0][r];
-        row[32] = z[1][r];
-      }
+      float* row = zs + (fperm(r) + 4 * h) * ZROW + HID + s;
+      row[0] = z[0][r];
+      row[32] = z[1][r];
     }
   }
   silu_tiles_t<K>(z, a);  // s2, edges on M
@@ -907,7 +907,7 @@ __device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const int32_t* pe
                                              int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
-  if (zs != nullptr && valid && h == 0) {
+  if (zs != nullptr && h == 0) {  // every slot (as fwd_tile)
     float* row = zs + s * ZROW + 2 * HID;
     float rw[2];
     __builtin_memcpy(rw, &g.r, sizeof(double));
