@@ -98,17 +98,20 @@ __device__ __forceinline__ float* stash_tile(float* zw, int q0, int qa) {
 // ------------------------------------------------------------------ forward
 // One 32-edge tile [q0, q0 + 32) of a unit: T += s2^T Y over the tile.  With a
 // stash tile zs, also its rows (edge slot k at zs + k ZROW).
-template <bool K = false>
+template <bool K = false, bool PAD = true>
 __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, const Recv& xi,
                                          const float* w1s, const float* w2s, float (*ysm)[NLM + 1],
                                          int q0, int qa, int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
   const BasisSeed sd = basis_seed(g.r, in.inv_rc, g.inv_r, h);
-  // Stash rows are written for all 32 slots, padding slots too (they hold the
-  // padding edge; the tile's 32 rows exist and slots past the unit's end are
-  // never read back), so no lane-dependent branch splits the stores.
-  if (zs != nullptr && h == 0) {
+  // With PAD, stash rows are written for all 32 slots, padding slots too
+  // (they hold the padding edge; the tile's 32 rows exist and slots past the
+  // unit's end are never read back), so no lane-dependent branch splits the
+  // stores: cheaper where tiles are full (one species).  Without PAD only the
+  // unit's own rows are written: less traffic where units are short and
+  // tiles half empty (several species).
+  if (zs != nullptr && h == 0 && (PAD || valid)) {
     float* row = zs + s * ZROW + 2 * HID;
     *reinterpret_cast<float4*>(row) = make_float4(g.ux, g.uy, g.uz, g.inv_r);
     *reinterpret_cast<float4*>(row + 4) = make_float4(sd.x, sd.xl, sd.s1, sd.c1);
@@ -122,7 +125,7 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
   if (zs != nullptr) {
     f32x16 d[2];
     silu_and_deriv_t<K>(z, a, d);  // s1 and silu'(z1), edges on N: hidden hid_k0(ks) + 4h
-    {
+    if (PAD || valid) {
       float* row = zs + s * ZROW + 4 * h;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -151,9 +154,12 @@ __device__ __forceinline__ void fwd_tile(const EdgeIn& in, const int32_t* perm, 
     // z2 rows: register r of tile m is edge slot fperm(r) + 4h, hidden 32 m + s
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float* row = zs + (fperm(r) + 4 * h) * ZROW + HID + s;
-      row[0] = z[0][r];
-      row[32] = z[1][r];
+      const int k = fperm(r) + 4 * h;
+      if (PAD || q0 + k < qb) {
+        float* row = zs + k * ZROW + HID + s;
+        row[0] = z[0][r];
+        row[32] = z[1][r];
+      }
     }
   }
   silu_tiles_t<K>(z, a);  // s2, edges on M
@@ -902,12 +908,13 @@ __device__ __forceinline__ void tab_horner(const float2* __restrict__ c, float t
   }
 }
 
+template <bool PAD = true>
 __device__ __forceinline__ void fwd_tile_tab(const EdgeIn& in, const int32_t* perm, const Recv& xi,
                                              const TabArgs& ta, float4* tp, float (*ysm)[NLM + 1], int q0, int qa,
                                              int qb, int s, int h, f32x4 T[4], float* zs) {
   const bool valid = q0 + s < qb;
   const Geo g = geo_from_raw(in, edge_raw(in, tile_edge(perm, q0, qa, qb, s)), xi.x);
-  if (zs != nullptr && h == 0) {  // every slot (as fwd_tile)
+  if (zs != nullptr && h == 0 && (PAD || valid)) {  // as fwd_tile
     float* row = zs + s * ZROW + 2 * HID;
     float rw[2];
     __builtin_memcpy(rw, &g.r, sizeof(double));
@@ -1285,9 +1292,9 @@ k_fold_multi(EdgeIn in, Units un, const int32_t* __restrict__ ord, const int32_t
       for (int q0 = qa; q0 < qb; q0 += 32, ++t) {
         float* zs = t < STASH_TILES ? zw + (size_t)t * 32 * ZROW : nullptr;
         if (TAB)
-          fwd_tile_tab(in, un.perm, xi, tab_pair(ta, p), tpb[wave], L.ysm, q0, qa, qb, s, h, T, zs);
+          fwd_tile_tab<false>(in, un.perm, xi, tab_pair(ta, p), tpb[wave], L.ysm, q0, qa, qb, s, h, T, zs);
         else
-          fwd_tile<K>(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, zs);
+          fwd_tile<K, false>(in, un.perm, xi, w1s, w2s, L.ysm, q0, qa, qb, s, h, T, zs);
       }
       float as[CPL][NLM];
       if (W3L)
