@@ -657,11 +657,27 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
 constexpr int GI_LD = 4 * HID + 4;
 constexpr int GRAM_FLOATS = HID * GI_LD;
 
-// G in global memory ([l][k][k']) into the interleaved LDS layout.
+// G in global memory ([l][k][k']) into the interleaved LDS layout, by a
+// workgroup of NT threads.  Thread t takes LDS entries t, t + NT, ... in LDS
+// order (row k, then 4 k' + l), so a wave's stores are consecutive words
+// (no bank conflicts), and issues all its loads before the first store (one
+// memory latency instead of one per entry; the loads of one instruction fall
+// in four 64-byte runs of G, one per degree).
+template <int NT>
 __device__ __forceinline__ void stage_gram(float* gs, const float* __restrict__ G) {
-  for (int t = threadIdx.x; t < 4 * HID * HID; t += blockDim.x) {
-    const int l = t >> 12, k = (t >> 6) & 63, kk = t & 63;
-    gs[k * GI_LD + 4 * kk + l] = G[t];
+  constexpr int NE = 4 * HID * HID, PER = NE / NT;
+  static_assert(NE % NT == 0, "whole entries per thread");
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = threadIdx.x + u * NT;
+    const int k = t >> 8, j = t & 255;  // j = 4 k' + l
+    v[u] = G[((j & 3) << 12) + (k << 6) + (j >> 2)];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = threadIdx.x + u * NT;
+    gs[(t >> 8) * GI_LD + (t & 255)] = v[u];
   }
 }
 
@@ -725,7 +741,7 @@ k_fold_fused(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
   stage_w12<64 * W>(wl, W1, W2, 0, KEXP);  // the scaled chain (KEXP)
-  stage_gram(gs, G);
+  stage_gram<64 * W>(gs, G);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
@@ -1164,7 +1180,7 @@ k_fold_table(EdgeIn in, Units un, TabArgs ta, const float* __restrict__ G, float
   const WaveLds<C> L(wbuf[wave]);
   const int N = un.n_atoms;
   const int nbp = (N + W - 1) / W;
-  stage_gram(gs, G);
+  stage_gram<64 * W>(gs, G);
   __syncthreads();
   for (int b = blockIdx.x; b < nbp; b += gridDim.x) {
     const int i = b * W + wave;
