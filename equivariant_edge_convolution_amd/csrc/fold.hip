@@ -624,7 +624,7 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
   const float* g0 = G + (size_t)l0 * HID * HID + lane;
   const float* g1 = G + (size_t)l1 * HID * HID + lane;
   float m0 = 0.f, m1 = 0.f;
-#pragma unroll 8
+#pragma unroll 16
   for (int kk = 0; kk < HID; ++kk) {
     m0 += g0[kk * HID] * tsm[kk][lm0];
     m1 += g1[kk * HID] * tsm[kk][lm1];
