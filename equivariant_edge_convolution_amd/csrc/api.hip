@@ -333,8 +333,16 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
                    model_span(m->W2, m, 2), model_span(m->W3, m, 3), model_span(m->emb, m, 4),
                    model_span(m->w_read, m, 5), tspan, lspan}));
   hipStream_t s = (hipStream_t)stream;
+  // phase events (the timed entry point): the first failed record is reported
+  hipError_t ev_err = hipSuccess;
   auto mark = [&](int k) {
-    if (events != nullptr && events[k] != nullptr) hipEventRecord((hipEvent_t)events[k], s);
+    if (events == nullptr || events[k] == nullptr) return;
+    const hipError_t e = hipEventRecord((hipEvent_t)events[k], s);
+    if (ev_err == hipSuccess) ev_err = e;
+  };
+  auto done = [&](const char* what) {
+    if (ev_err != hipSuccess) return fail(EEC_ERR_HIP, std::string(what) + ": event record: " + hipGetErrorString(ev_err));
+    return launched(what);
   };
   char* ws = (char*)workspace;
   if (noalloc) TRY(scratch_on_current_device(s, &ws));
@@ -369,7 +377,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     mark(2 * EEC_PHASE_SCATTER);
     launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
     mark(2 * EEC_PHASE_SCATTER + 1);
-    return launched("energy_forces_tabulated");
+    return done("energy_forces_tabulated");
   }
   if (folded && fold_fused_supported(p)) {
     // one kernel per receiver from geometry to dE/dd; no preparation, no A
@@ -386,7 +394,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     mark(2 * EEC_PHASE_SCATTER);
     launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
     mark(2 * EEC_PHASE_SCATTER + 1);
-    return launched("energy_forces");
+    return done("energy_forces");
   }
   if (folded && fold_multi_supported(p)) {
     // one kernel per call from geometry to dE/dd, sender species after species
@@ -404,7 +412,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
     mark(2 * EEC_PHASE_SCATTER);
     launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
     mark(2 * EEC_PHASE_SCATTER + 1);
-    return launched("energy_forces");
+    return done("energy_forces");
   }
   mark(2 * EEC_PHASE_PREPARE);
   launch_prepare(s, p, g, species, ws, A);
@@ -438,7 +446,7 @@ static eec_status energy_forces_impl(void* stream, const eec_graph* g, const dou
   mark(2 * EEC_PHASE_SCATTER);
   launch_scatter(s, p, g, pos, b, gbuf, forces, ei, energy, virial, ws);
   mark(2 * EEC_PHASE_SCATTER + 1);
-  return launched("energy_forces");
+  return done("energy_forces");
 }
 
 eec_status eec_energy_forces(void* stream, const eec_graph* g, const double* pos, const double* box,

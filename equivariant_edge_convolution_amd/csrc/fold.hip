@@ -393,7 +393,7 @@ __device__ __forceinline__ void bwd_tile(const EdgeIn& in, const Recv& xi, const
     g.uz = u.z;
     g.inv_r = u.w;
     sd = basis_seed_stored(bs.x, bs.y, bs.z, bs.w, u.w, h);
-    f32x16 z[2], s1[2];
+    f32x16 z[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll

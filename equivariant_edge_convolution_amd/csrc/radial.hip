@@ -142,7 +142,7 @@ template <int W>
 __global__ void __launch_bounds__(64 * W)
 k_forward(EdgeIn in, Units un, const float* __restrict__ W1, const float* __restrict__ W2,
           const float* __restrict__ W3, const float* __restrict__ emb, float* __restrict__ A_out) {
-  constexpr int C = 64, NC = 256;
+  constexpr int C = 64;
   constexpr int LD3 = Lds<C>::LD3;
   __shared__ float lds[Lds<C>::FLOATS];
   __shared__ float ysm[W][32][NLM + 1];  // one padding column against bank conflicts
@@ -252,7 +252,6 @@ __global__ void __launch_bounds__(64 * W)
 k_backward(EdgeIn in, Sched sc, const float* __restrict__ W1, const float* __restrict__ W2,
            const float* __restrict__ W3, const float* __restrict__ emb, int n_species,
            const float* __restrict__ Abar, float* __restrict__ gout) {
-  constexpr int NC = Lds<C>::NC;
   __shared__ float lds[Lds<C>::FLOATS];
   __shared__ SchedState st;
   sched_init<W>(sc, st);
