@@ -641,6 +641,78 @@ __device__ __forceinline__ float gram_epilogue_split(float* tw, const float* wba
   return 0.5f * e * scale;
 }
 
+// The same for the two receivers of a pair at once (the second only when
+// `two`): the partial T of receiver r summed into tw[r], then each wave's two
+// harmonics of both receivers from one pass over its rows of G (both
+// receivers share them), so the L2 latency of those loads is paid once per
+// pair.  Each receiver's sums run in the same order as above.  E_i of the
+// receivers into e[0], e[1].
+template <int W, int TSM_OFF, int STRIDE>
+__device__ __forceinline__ void gram_epilogue_pair(float* tw0, const float* wbase, float* tw1, bool two,
+                                                   const float* __restrict__ G, int lane, int wave,
+                                                   float (*msh0)[HID + 1], float (*msh1)[HID + 1],
+                                                   float (*esh)[W], float scale, float e[2]) {
+  static_assert(W == 8, "two harmonics per wave");
+  for (int x = threadIdx.x; x < HID * NLM; x += 64 * W) {
+    float v = tw0[x];
+#pragma unroll
+    for (int w = 1; w < W; ++w) v += wbase[w * STRIDE + TSM_OFF + x];
+    tw0[x] = v;
+    if (two) {
+      float u = tw1[x];
+#pragma unroll
+      for (int w = 1; w < W; ++w) u += tw1[w * HID * NLM + x];
+      tw1[x] = u;
+    }
+  }
+  __syncthreads();
+  const float(*t0)[NLM] = reinterpret_cast<const float(*)[NLM]>(tw0);
+  const float(*t1)[NLM] = reinterpret_cast<const float(*)[NLM]>(tw1);
+  const int lm0 = 2 * wave, lm1 = lm0 + 1;
+  const int l0 = lm0 == 0 ? 0 : (lm0 < 4 ? 1 : (lm0 < 9 ? 2 : 3));
+  const int l1 = lm1 < 4 ? 1 : (lm1 < 9 ? 2 : 3);
+  const float* g0 = G + (size_t)l0 * HID * HID + lane;
+  const float* g1 = G + (size_t)l1 * HID * HID + lane;
+  float m00 = 0.f, m01 = 0.f, m10 = 0.f, m11 = 0.f;
+  if (two) {
+#pragma unroll 16
+    for (int kk = 0; kk < HID; ++kk) {
+      const float a = g0[kk * HID], b = g1[kk * HID];
+      m00 += a * t0[kk][lm0];
+      m01 += b * t0[kk][lm1];
+      m10 += a * t1[kk][lm0];
+      m11 += b * t1[kk][lm1];
+    }
+  } else {
+#pragma unroll 16
+    for (int kk = 0; kk < HID; ++kk) {
+      m00 += g0[kk * HID] * t0[kk][lm0];
+      m01 += g1[kk * HID] * t0[kk][lm1];
+    }
+  }
+  msh0[lm0][lane] = m00 * scale;
+  msh0[lm1][lane] = m01 * scale;
+  float es0 = t0[lane][lm0] * m00 + t0[lane][lm1] * m01;
+  for (int off = 32; off > 0; off >>= 1) es0 += __shfl_xor(es0, off);
+  if (lane == 0) esh[0][wave] = es0;
+  if (two) {
+    msh1[lm0][lane] = m10 * scale;
+    msh1[lm1][lane] = m11 * scale;
+    float es1 = t1[lane][lm0] * m10 + t1[lane][lm1] * m11;
+    for (int off = 32; off > 0; off >>= 1) es1 += __shfl_xor(es1, off);
+    if (lane == 0) esh[1][wave] = es1;
+  }
+  __syncthreads();
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    s0 += esh[0][w];
+    s1 += two ? esh[1][w] : 0.f;
+  }
+  e[0] = 0.5f * s0 * scale;
+  e[1] = 0.5f * s1 * scale;
+}
+
 // ------------------------------------------------------------------ fused (one species)
 // With one species, receiver i's unit holds its whole row, and the backward of
 // the unit needs only M_i, which depends on nothing but the unit's own forward:
@@ -798,7 +870,7 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
   __shared__ __align__(16) float wbuf[W][FoldLds<C>::FUSED];
   __shared__ __align__(16) float tsm2[W][HID * NLM];  // the waves' partial T of the second receiver
   __shared__ __align__(16) float msh[2][NLM][HID + 1];  // M of the two receivers, read by every wave
-  __shared__ float esh[W];
+  __shared__ float esh2[2][W];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const WaveLds<C> L(wbuf[wave]);
   const float* w1s = w12;
@@ -846,14 +918,14 @@ k_fold_split(EdgeIn in, Units un, const float* __restrict__ W1, const float* __r
     if (i1 < N) put_t(T, tsm2[wave]);
     __syncthreads();
     {
-      const float e2 = gram_epilogue_split<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(
-          &wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], G, lane, wave, msh[0], esh, KEXP_INV2);
-      if (threadIdx.x == 0) ei[i0] = e2;
-    }
-    if (i1 < N) {
-      const float e2 = gram_epilogue_split<W, 0, HID * NLM>(&tsm2[0][0], &tsm2[0][0], G, lane, wave, msh[1], esh,
-                                                            KEXP_INV2);
-      if (threadIdx.x == 0) ei[i1] = e2;
+      float e2[2];
+      gram_epilogue_pair<W, FoldLds<C>::TSM, FoldLds<C>::FUSED>(&wbuf[0][FoldLds<C>::TSM], &wbuf[0][0], &tsm2[0][0],
+                                                                 i1 < N, G, lane, wave, msh[0], msh[1], esh2,
+                                                                 KEXP_INV2, e2);
+      if (threadIdx.x == 0) {
+        ei[i0] = e2[0];
+        if (i1 < N) ei[i1] = e2[1];
+      }
     }
     __syncthreads();
     j = 0;
