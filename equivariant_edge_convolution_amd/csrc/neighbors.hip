@@ -87,7 +87,11 @@ __global__ void k_nb_bin(int32_t n, const double* __restrict__ pos, double Lx, d
 }
 
 // Exclusive scan of n unsigned counts into out[0..n] (out[n] = total) with one
-// workgroup of 1024 threads; also stores the total as int64 when asked.
+// workgroup of 1024 threads, each a contiguous slice; also stores the total as
+// int64 when asked.  A slice of at most SCAN_REG counts (n up to 32 Ki) is
+// loaded with all its loads in flight and kept in registers, instead of one
+// load waited on per count.
+constexpr int SCAN_REG = 32;
 __global__ void __launch_bounds__(1024) k_scan_excl(const uint32_t* __restrict__ in, int64_t n,
                                                     int32_t* __restrict__ out,
                                                     int64_t* __restrict__ total) {
@@ -95,8 +99,19 @@ __global__ void __launch_bounds__(1024) k_scan_excl(const uint32_t* __restrict__
   const int t = threadIdx.x;
   const int64_t per = (n + 1023) / 1024;
   const int64_t a = std::min<int64_t>(n, t * per), b = std::min<int64_t>(n, a + per);
+  const bool reg = per <= SCAN_REG;  // uniform over the workgroup
+  uint32_t v[SCAN_REG];
   int64_t s = 0;
-  for (int64_t k = a; k < b; ++k) s += in[k];
+  const int m = (int)(b - a);  // at most SCAN_REG when reg
+  if (reg) {
+    const uint32_t* src = in + a;
+#pragma unroll
+    for (int u = 0; u < SCAN_REG; ++u) v[u] = u < m ? src[u] : 0u;
+#pragma unroll
+    for (int u = 0; u < SCAN_REG; ++u) s += v[u];
+  } else {
+    for (int64_t k = a; k < b; ++k) s += in[k];
+  }
   part[t] = s;
   __syncthreads();
   // Hillis-Steele inclusive scan over the 1024 thread sums (fixed order).
@@ -107,9 +122,19 @@ __global__ void __launch_bounds__(1024) k_scan_excl(const uint32_t* __restrict__
     __syncthreads();
   }
   int64_t run = part[t] - s;
-  for (int64_t k = a; k < b; ++k) {
-    out[k] = (int32_t)run;
-    run += in[k];
+  if (reg) {
+    int32_t* dst = out + a;
+#pragma unroll
+    for (int u = 0; u < SCAN_REG; ++u)
+      if (u < m) {
+        dst[u] = (int32_t)run;
+        run += v[u];
+      }
+  } else {
+    for (int64_t k = a; k < b; ++k) {
+      out[k] = (int32_t)run;
+      run += in[k];
+    }
   }
   if (t == 1023) {
     out[n] = (int32_t)part[1023];
