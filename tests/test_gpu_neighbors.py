@@ -45,6 +45,24 @@ def test_csr_bit_exact_dense_rows(n_atoms):
     assert np.array_equal(np_(g.rev), ref.rev)
 
 
+def test_csr_bit_exact_more_than_32k_atoms():
+    # 40,000 random atoms in a 100 A box (about 36 edges a row): more row counts
+    # than the scan keeps in registers (32 per thread of 1,024), so the scan
+    # takes its slice-by-slice path
+    say("[neighbors] 40,000 atoms")
+    box = np.full(3, 100.0)
+    cfg = I.make_cluster(np.random.default_rng(40000).uniform(0.0, 100.0, (40000, 3)), box)
+    pos = torch.as_tensor(cfg.pos).to(DEV)
+    g = B.build_neighbors(pos, box, 6.0)
+    ref = N.neighbors_celllist(cfg.pos, box, 6.0)
+    assert ref.n_edges > 1_000_000
+    assert g.n_edges == ref.n_edges
+    assert np.array_equal(np_(g.row_ptr), ref.row_ptr)
+    assert np.array_equal(np_(g.col), ref.col)
+    assert np.array_equal(np_(g.shift), ref.shift)
+    assert np.array_equal(np_(g.rev), ref.rev)
+
+
 def test_repeat_is_identical():
     cfg = I.make_config("PV3")
     pos, species, _ = device_inputs(cfg)
